@@ -1,0 +1,11 @@
+"""CPU oracle for the KDA forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never does; it shares no code with
+it.  Contents:
+
+  kda_oracle.c / recurrent.py   token-by-token fp64 recurrence (the definition)
+  chunked.py                    fp64 chunked re-derivation of the same result
+"""
+from .recurrent import OracleLib, decode, lib_path, num_threads, prefill  # noqa: F401
+from .chunked import chunked_prefill, unit_lower_inverse  # noqa: F401

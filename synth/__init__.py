@@ -1,0 +1,15 @@
+"""Seeded synthetic inputs for KDA prefill and decode.
+
+This package only draws random numbers and rounds them to storage dtypes.  It
+holds none of the attention arithmetic, so the CPU oracle and the HIP path can
+both consume its output without sharing any of the method.
+"""
+from .kda_inputs import (  # noqa: F401
+    CONFIGS,
+    KdaInputs,
+    bf16_bits_to_f64,
+    f64_to_bf16_bits,
+    make_config,
+    make_inputs,
+    slice_heads,
+)

@@ -1,0 +1,47 @@
+"""The seeded input generator: determinism, stream independence and the
+rounding to bf16.  No GPU."""
+import numpy as np
+import torch
+
+import synth
+
+
+def test_deterministic_and_stream_keyed():
+    a = synth.make_inputs(7, [10, 5], 2, 8, dtype="bf16")
+    b = synth.make_inputs(7, [10, 5], 2, 8, dtype="bf16")
+    for name in ["q", "k", "v", "g", "beta"]:
+        assert np.array_equal(getattr(a, name), getattr(b, name))
+    c = synth.make_inputs(7, [10, 5], 2, 8, dtype="bf16", h0_std=0.02)
+    assert np.array_equal(a.q, c.q) and c.h0 is not None and a.h0 is None
+
+
+def test_bf16_rounding_is_rne():
+    """fp64 -> bf16 rounding agrees with torch's fp32 -> bf16 (round to nearest
+    even) on values that are exact in fp32, including exact ties."""
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(100000).astype(np.float32)
+    ties = (np.arange(1, 200, dtype=np.float32) * 2.0 ** -7 + 2.0 ** -9).astype(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    mine = synth.f64_to_bf16_bits(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    back = synth.bf16_bits_to_f64(mine)
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -8)
+
+
+def test_config_shapes_and_ranges():
+    inp = synth.make_config(0)
+    assert inp.q.shape == (128, 2, 32) and inp.q.dtype == np.float32 and inp.chunk == 16
+    assert np.all(inp.g <= 0)
+    n = np.linalg.norm(inp.q.astype(np.float64), axis=-1)
+    assert np.allclose(n, 1.0, atol=1e-6)
+    lens = synth.kda_inputs.config_lengths(3)
+    assert len(lens) == 8 and all(300 <= x <= 8192 for x in lens)
+    assert lens == synth.kda_inputs.config_lengths(3)
+
+
+def test_kimi_gate_is_negative():
+    inp = synth.make_inputs(3, [100], 4, 16, dtype="bf16", gate="kimi")
+    assert np.all(inp.g <= 0) and np.all(np.isfinite(inp.g))
+    b = synth.bf16_bits_to_f64(inp.beta)
+    assert np.all((b > 0) & (b < 1))
