@@ -1,0 +1,148 @@
+"""ctypes mirror of include/kda.h.  Loads the in-tree libkda.so; there is no
+other implementation to fall back to, so a missing library is an error."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_ABI_VERSION = 1
+KDA_OK = 0
+KDA_ERR_NULL = -1
+KDA_ERR_SHAPE = -2
+KDA_ERR_DTYPE = -3
+KDA_ERR_UNSUPPORTED = -4
+KDA_ERR_ALIGN = -5
+KDA_ERR_WORKSPACE = -6
+KDA_ERR_HIP = -7
+KDA_ERR_VERSION = -8
+KDA_ERR_ALIAS = -9
+KDA_ERR_SEQLENS = -10
+
+KDA_DTYPE_F32 = 1
+KDA_DTYPE_BF16 = 2
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("n_seqs", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("t_total", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("ht", ctypes.c_void_p),
+    ]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("n_seqs", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("dk", ctypes.c_int32),
+        ("dv", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("state", ctypes.c_void_p),
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+    ]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status}"
+                         + (f", hipError {lib().kda_last_hip_error()})" if status == KDA_ERR_HIP
+                            else ")"))
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -m gated_delta_rule_55_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kda_abi_version.argtypes = []
+        L.kda_abi_version.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_hip_error.argtypes = []
+        L.kda_last_hip_error.restype = ctypes.c_int
+        L.kda_chunk_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillDesc),
+                                                        ctypes.POINTER(ctypes.c_int)]
+        L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.kda_chunk_prefill.restype = ctypes.c_int
+        L.kda_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.kda_workspace_status.restype = ctypes.c_int
+        L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.c_void_p]
+        L.kda_recurrent_decode.restype = ctypes.c_int
+        if L.kda_abi_version() != KDA_ABI_VERSION:
+            raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != {KDA_ABI_VERSION}")
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def prefill_desc(**kw) -> PrefillDesc:
+    d = PrefillDesc()
+    d.struct_size = ctypes.sizeof(PrefillDesc)
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+def decode_desc(**kw) -> DecodeDesc:
+    d = DecodeDesc()
+    d.struct_size = ctypes.sizeof(DecodeDesc)
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+def workspace_bytes(desc: PrefillDesc) -> int:
+    st = ctypes.c_int(0)
+    n = lib().kda_chunk_prefill_workspace_bytes(ctypes.byref(desc), ctypes.byref(st))
+    if st.value != KDA_OK:
+        raise KdaError(st.value, "kda_chunk_prefill_workspace_bytes")
+    return int(n)
+
+
+def chunk_prefill_raw(desc: PrefillDesc, workspace: int, workspace_bytes: int, stream: int) -> int:
+    return int(lib().kda_chunk_prefill(ctypes.byref(desc), workspace, workspace_bytes, stream))
+
+
+def recurrent_decode_raw(desc: DecodeDesc, stream: int) -> int:
+    return int(lib().kda_recurrent_decode(ctypes.byref(desc), stream))
+
+
+def workspace_status(workspace: int, stream: int) -> int:
+    return int(lib().kda_workspace_status(workspace, stream))

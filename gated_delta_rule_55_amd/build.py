@@ -1,0 +1,70 @@
+"""Build libkda.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+
+Usage: python -m gated_delta_rule_55_amd.build [-v]
+"""
+import os
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(PKG, "libkda.so")
+SOURCES = ["kda_abi.cpp", "kda_decode.hip", "kda_prefill.hip"]
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # Packed-fp32 instructions are kept out of every kernel (the host pass
+    # ignores the feature with a warning).
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def _hipcc():
+    p = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    return p if os.path.exists(p) else "hipcc"
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs, objs = [], []
+    t0 = time.time()
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        cmd = [_hipcc()] + HIPCC_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        while sum(p.poll() is None for _, p in procs) >= jobs:
+            time.sleep(0.1)
+    failed = False
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # the host pass warns that it does not know the packed-fp32 feature
+        lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+        if lines:
+            print(f"[{src}]\n" + "\n".join(lines), flush=True)
+        if p.returncode != 0:
+            failed = True
+    if failed:
+        raise RuntimeError("hipcc failed")
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", OUT + ".tmp"] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(OUT + ".tmp", OUT)
+    if verbose:
+        print(f"built {OUT} in {time.time() - t0:.1f}s", flush=True)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

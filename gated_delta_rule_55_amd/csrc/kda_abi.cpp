@@ -1,0 +1,216 @@
+// kda_abi.cpp -- the C ABI declared in include/kda.h: descriptor validation on
+// the host, workspace sizing, and launches on the caller's stream.
+//
+// Every check runs before anything is enqueued (page "model(kimi_linear):
+// ONE-SURFACE ROW 7 -- fold Kimi-Linear onto the shared paged runner",
+// section Landed: an explicit choice that cannot be honoured fails loudly
+// instead of being replaced).  The library reads no environment variables.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  g_last_hip_error = (int)e;
+  return KDA_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = (uintptr_t)p;
+  return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Shared checks of the prefill descriptor; fills `a` on success.
+int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->struct_size != sizeof(kda_prefill_desc)) return KDA_ERR_VERSION;
+  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE;
+  if (d->n_seqs < 1 || d->n_heads < 1 || d->n_heads > 65535 || d->t_total < 0 ||
+      d->t_total > INT32_MAX - 64)
+    return KDA_ERR_SHAPE;
+  if (d->dk != d->dv || !supported_d(d->dk)) return KDA_ERR_UNSUPPORTED;
+  const int chunk = d->chunk == 0 ? 64 : d->chunk;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_supported(d->dtype == KDA_DTYPE_BF16, d->dk, chunk)) return KDA_ERR_UNSUPPORTED;
+  if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
+  a->bf16 = d->dtype == KDA_DTYPE_BF16;
+  a->n_seqs = d->n_seqs;
+  a->n_heads = d->n_heads;
+  a->d = d->dk;
+  a->chunk = chunk;
+  a->t_total = d->t_total;
+  a->scale = d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  a->q = d->q;
+  a->k = d->k;
+  a->v = d->v;
+  a->g = d->g;
+  a->beta = d->beta;
+  a->h0 = d->h0;
+  a->cu_seqlens = d->cu_seqlens;
+  a->o = d->o;
+  a->ht = d->ht;
+  return KDA_OK;
+}
+
+int check_prefill_pointers(const kda_prefill_desc* d, const kda::PrefillArgs& a) {
+  if (!d->cu_seqlens && d->n_seqs != 1) return KDA_ERR_NULL;
+  if (d->t_total > 0 && (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->o))
+    return KDA_ERR_NULL;
+  // q and k rows are read as 16-byte vectors; everything else element-wise.
+  const uintptr_t es_al = d->dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  if ((d->q && !aligned(d->q, 16)) || (d->k && !aligned(d->k, 16))) return KDA_ERR_ALIGN;
+  const void* pe[] = {d->v, d->beta, d->o};
+  for (const void* p : pe)
+    if (p && !aligned(p, es_al)) return KDA_ERR_ALIGN;
+  const void* p4[] = {d->g, d->h0, d->ht, d->cu_seqlens};
+  for (const void* p : p4)
+    if (p && !aligned(p, 4)) return KDA_ERR_ALIGN;
+
+  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
+  const Range rq = range_of(d->q, T * H * D * es), rk = range_of(d->k, T * H * D * es),
+              rv = range_of(d->v, T * H * D * es), rg = range_of(d->g, T * H * D * 4),
+              rb = range_of(d->beta, T * H * es), ro = range_of(d->o, T * H * D * es),
+              rh0 = range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
+              rht = range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
+              rcu = range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0);
+  const Range inputs[] = {rq, rk, rv, rg, rb, rh0, rcu};
+  for (const Range& r : inputs)
+    if (overlap(ro, r)) return KDA_ERR_ALIAS;
+  if (overlap(ro, rht)) return KDA_ERR_ALIAS;
+  // ht may be exactly h0 (in-place carry) but may not partly overlap it, nor
+  // overlap any other input.
+  if (d->ht && d->h0 && d->ht != d->h0 && overlap(rht, rh0)) return KDA_ERR_ALIAS;
+  const Range others[] = {rq, rk, rv, rg, rb, rcu};
+  for (const Range& r : others)
+    if (overlap(rht, r)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "required pointer is NULL";
+    case KDA_ERR_SHAPE: return "size out of range";
+    case KDA_ERR_DTYPE: return "unknown dtype";
+    case KDA_ERR_UNSUPPORTED: return "head dim or chunk size not supported";
+    case KDA_ERR_ALIGN: return "pointer misaligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_HIP: return "HIP launch failed";
+    case KDA_ERR_VERSION: return "descriptor struct_size mismatch";
+    case KDA_ERR_ALIAS: return "output overlaps an input";
+    case KDA_ERR_SEQLENS: return "cu_seqlens content invalid";
+    default: return "unknown status";
+  }
+}
+
+int kda_last_hip_error(void) { return g_last_hip_error; }
+
+size_t kda_chunk_prefill_workspace_bytes(const kda_prefill_desc* d, int* status) {
+  kda::PrefillArgs a;
+  const int st = check_prefill(d, &a);
+  if (status) *status = st;
+  if (st != KDA_OK) return 0;
+  return kda::prefill_workspace_bytes(a);
+}
+
+int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  kda::PrefillArgs a;
+  int st = check_prefill(d, &a);
+  if (st != KDA_OK) return st;
+  st = check_prefill_pointers(d, a);
+  if (st != KDA_OK) return st;
+  const size_t need = kda::prefill_workspace_bytes(a);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
+  const Range rw = range_of(workspace, (int64_t)need);
+  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
+  const Range touched[] = {range_of(d->q, T * H * D * es), range_of(d->k, T * H * D * es),
+                           range_of(d->v, T * H * D * es), range_of(d->g, T * H * D * 4),
+                           range_of(d->beta, T * H * es), range_of(d->o, T * H * D * es),
+                           range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
+                           range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
+                           range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0)};
+  for (const Range& r : touched)
+    if (overlap(rw, r)) return KDA_ERR_ALIAS;
+  return hip_status(kda::launch_prefill(a, workspace, (hipStream_t)stream));
+}
+
+int kda_workspace_status(const void* workspace, void* stream) {
+  if (!workspace) return KDA_ERR_NULL;
+  int host = 0;
+  const unsigned char* p = static_cast<const unsigned char*>(workspace) + kda::kWsStatusOffset;
+  hipError_t e = hipMemcpyAsync(&host, p, sizeof(int), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e);
+  return host;
+}
+
+int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->struct_size != sizeof(kda_decode_desc)) return KDA_ERR_VERSION;
+  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE;
+  if (d->n_seqs < 0 || d->n_heads < 1 || (int64_t)d->n_seqs * d->n_heads > INT32_MAX)
+    return KDA_ERR_SHAPE;
+  if (d->dk != d->dv || !supported_d(d->dk)) return KDA_ERR_UNSUPPORTED;
+  if (!std::isfinite(d->scale)) return KDA_ERR_SHAPE;
+  if (d->n_seqs == 0) return KDA_OK;
+  if (!d->state || !d->q || !d->k || !d->v || !d->g || !d->beta || !d->o) return KDA_ERR_NULL;
+  const bool bf = d->dtype == KDA_DTYPE_BF16;
+  // the state is read and written as 16-byte vectors; the rest element-wise
+  if (!aligned(d->state, 16) || !aligned(d->g, 4)) return KDA_ERR_ALIGN;
+  const void* pe[] = {d->q, d->k, d->v, d->beta, d->o};
+  for (const void* p : pe)
+    if (!aligned(p, bf ? 2 : 4)) return KDA_ERR_ALIGN;
+  const int64_t es = bf ? 2 : 4, NH = (int64_t)d->n_seqs * d->n_heads, D = d->dk;
+  const Range ro = range_of(d->o, NH * D * es);
+  const Range ins[] = {range_of(d->state, NH * D * D * 4), range_of(d->q, NH * D * es),
+                       range_of(d->k, NH * D * es),        range_of(d->v, NH * D * es),
+                       range_of(d->g, NH * D * 4),         range_of(d->beta, NH * es)};
+  for (const Range& r : ins)
+    if (overlap(ro, r)) return KDA_ERR_ALIAS;
+  for (int i = 1; i < 6; ++i)
+    if (overlap(ins[0], ins[i])) return KDA_ERR_ALIAS;
+  kda::DecodeArgs a;
+  a.bf16 = bf;
+  a.n_seqs = d->n_seqs;
+  a.n_heads = d->n_heads;
+  a.d = d->dk;
+  a.scale = d->scale != 0.f ? d->scale : 1.0f / std::sqrt((float)d->dk);
+  a.state = d->state;
+  a.q = d->q;
+  a.k = d->k;
+  a.v = d->v;
+  a.g = d->g;
+  a.beta = d->beta;
+  a.o = d->o;
+  return hip_status(kda::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

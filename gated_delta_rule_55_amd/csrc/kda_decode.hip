@@ -1,0 +1,124 @@
+// kda_decode.hip -- recurrent KDA decode: one token per (sequence, head) on a
+// carried fp32 state, updated in place.
+//
+// The decode form is the token recurrence itself, run once per call from the
+// state the caller passes ("prefill once, then advance one token per step from
+// the carried state"; page "Kimi-Linear: paged-incremental decode
+// (prefill-once + carried-state decode)", squash commit).  Per (n, h):
+//     S' = Diag(exp(g)) S                 decay of each key-channel row
+//     p  = S'^T k,  r = S'^T q            two column reductions over dk
+//     u  = beta (v - p)                   delta-rule error
+//     S  = S' + k u^T                     write
+//     o  = scale (r + (k . q) u)          = scale S^T q after the write
+//
+// The step reads the state once and writes it once; it is bound by HBM
+// bandwidth (a few flops per state byte), so the kernel is arranged for that:
+// one 256-thread workgroup per (n, h); thread (rg, cq) owns four consecutive
+// value columns (one 16-byte vector) of D / RG rows; 32 threads cover one
+// 512-byte row so every load and store is a full coalesced row segment.  All
+// of a thread's state loads are issued before any arithmetic, the two column
+// reductions go through LDS, and the updated rows are stored from registers.
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+template <typename TIO, int D>
+__global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
+                                                     const TIO* __restrict__ q,
+                                                     const TIO* __restrict__ k,
+                                                     const TIO* __restrict__ v,
+                                                     const float* __restrict__ g,
+                                                     const TIO* __restrict__ beta,
+                                                     TIO* __restrict__ o, float scale) {
+  constexpr int NQ = D / 4;       // column quads per row
+  constexpr int RG = 256 / NQ;    // row groups
+  constexpr int RPT = D / RG;     // rows per thread
+  static_assert(NQ * RG == 256 && RG * RPT == D, "decode tiling");
+
+  __shared__ float s_q[D], s_k[D], s_d[D], s_u[D];
+  __shared__ float s_red[2][RG][D];
+  __shared__ float s_kq;
+
+  const int tid = threadIdx.x;
+  const int cq = tid % NQ;
+  const int rg = tid / NQ;
+  const int64_t nh = blockIdx.x;
+  float* S = state + nh * (int64_t)(D * D);
+
+  // Issue every state load first: rows rg + RG * i, columns 4cq .. 4cq + 3.
+  f32x4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = *reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + 4 * cq);
+
+  if (tid < D) {
+    s_q[tid] = to_f32(q[nh * D + tid]);
+    s_k[tid] = to_f32(k[nh * D + tid]);
+    s_d[tid] = __expf(g[nh * D + tid]);
+  }
+  __syncthreads();
+  if (tid < 64) {  // k . q by one wave
+    float acc = 0.f;
+    for (int i = tid; i < D; i += 64) acc += s_k[i] * s_q[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (tid == 0) s_kq = acc;
+  }
+
+  f32x4 pk = zero4(), pq = zero4();
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + RG * i;
+    s[i] *= s_d[r];
+    pk += s[i] * s_k[r];
+    pq += s[i] * s_q[r];
+  }
+  *reinterpret_cast<f32x4*>(&s_red[0][rg][4 * cq]) = pk;
+  *reinterpret_cast<f32x4*>(&s_red[1][rg][4 * cq]) = pq;
+  __syncthreads();
+
+  if (tid < D) {
+    float p = 0.f, r = 0.f;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      p += s_red[0][j][tid];
+      r += s_red[1][j][tid];
+    }
+    const float b = to_f32(beta[nh]);
+    const float u = b * (to_f32(v[nh * D + tid]) - p);
+    s_u[tid] = u;
+    o[nh * D + tid] = from_f32<TIO>(scale * (r + s_kq * u));
+  }
+  __syncthreads();
+
+  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + RG * i;
+    *reinterpret_cast<f32x4*>(S + r * D + 4 * cq) = s[i] + s_k[r] * u4;
+  }
+}
+
+template <typename TIO, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
+  hipLaunchKernelGGL((decode_kernel<TIO, D>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                     a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
+                     (const TIO*)a.beta, (TIO*)a.o, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if ((int64_t)a.n_seqs * a.n_heads == 0) return hipSuccess;
+  const bool bf = a.bf16;
+  switch (a.d) {
+    case 32: return bf ? launch_decode_t<bf16, 32>(a, stream) : launch_decode_t<float, 32>(a, stream);
+    case 64: return bf ? launch_decode_t<bf16, 64>(a, stream) : launch_decode_t<float, 64>(a, stream);
+    case 128:
+      return bf ? launch_decode_t<bf16, 128>(a, stream) : launch_decode_t<float, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kda

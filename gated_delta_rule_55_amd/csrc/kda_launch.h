@@ -1,0 +1,50 @@
+// kda_launch.h -- internal interface between the C ABI (kda_abi.cpp) and the
+// kernel launchers.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  bool bf16;
+  int n_seqs, n_heads, d;
+  float scale;
+  float* state;
+  const void *q, *k, *v;
+  const float* g;
+  const void* beta;
+  void* o;
+};
+
+struct PrefillArgs {
+  bool bf16;
+  int n_seqs, n_heads, d, chunk;
+  int64_t t_total;
+  float scale;
+  const void *q, *k, *v;
+  const float* g;
+  const void* beta;
+  const float* h0;
+  const int32_t* cu_seqlens;  // may be NULL when n_seqs == 1
+  void* o;
+  float* ht;
+};
+
+// Upper bound on the number of chunks: sum_n ceil(L_n / C) <= T / C + N.
+inline int64_t max_chunks(int64_t t_total, int n_seqs, int chunk) {
+  return t_total / chunk + n_seqs;
+}
+
+// Whether the (dtype, head dim, chunk) instance is built.
+bool prefill_supported(bool bf16, int d, int chunk);
+size_t prefill_workspace_bytes(const PrefillArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Offset of the device status word inside a prefill workspace.
+constexpr size_t kWsStatusOffset = 0;
+
+}  // namespace kda

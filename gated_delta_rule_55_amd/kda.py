@@ -1,0 +1,138 @@
+"""PyTorch-facing entry points of libkda: argument marshalling only.
+
+Every step of the KDA forward runs in the HIP kernels behind the C ABI
+(include/kda.h); torch supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _abi
+
+_DTYPES = {torch.float32: _abi.KDA_DTYPE_F32, torch.bfloat16: _abi.KDA_DTYPE_BF16}
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
+                 ht=None) -> _abi.PrefillDesc:
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    return _abi.prefill_desc(
+        dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv, chunk=int(chunk),
+        t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
+        v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
+        o=_ptr(o), ht=_ptr(ht))
+
+
+def prefill_workspace_bytes(T: int, H: int, d: int, n_seqs: int = 1, chunk: int = 64,
+                            dtype: torch.dtype = torch.bfloat16) -> int:
+    desc = _abi.prefill_desc(dtype=_DTYPES[dtype], n_seqs=n_seqs, n_heads=H, dk=d, dv=d,
+                             chunk=chunk, t_total=T)
+    return _abi.workspace_bytes(desc)
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                  chunk: int = 64, out: Optional[torch.Tensor] = None,
+                  ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, stream=None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
+    h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
+    None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
+    `ht` may be h0 itself (in-place carry)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_prefill runs on the GPU only")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    _check(k, "k", (T, H, dk), q.dtype, dev)
+    _check(v, "v", (T, H, dv), q.dtype, dev)
+    _check(g, "g", (T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (T, H), q.dtype, dev)
+    _check(q, "q", (T, H, dk), q.dtype, dev)
+    if h0 is not None:
+        _check(h0, "h0", (N, H, dk, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (T, H, dv), q.dtype, dev)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif ht is not None:
+        _check(ht, "ht", (N, H, dk, dv), torch.float32, dev)
+    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht)
+    need = _abi.workspace_bytes(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _abi.chunk_prefill_raw(desc, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != _abi.KDA_OK:
+        raise _abi.KdaError(st, "kda_chunk_prefill")
+    return out, ht
+
+
+def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     g: torch.Tensor, beta: torch.Tensor, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One recurrent decode step; `state` [N, H, dk, dv] fp32 is updated in place.
+    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].  Returns o [N, H, dv]."""
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("recurrent_decode runs on the GPU only")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    N, H, dk, dv = state.shape
+    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    _check(q, "q", (N, H, dk), q.dtype, dev)
+    _check(k, "k", (N, H, dk), q.dtype, dev)
+    _check(v, "v", (N, H, dv), q.dtype, dev)
+    _check(g, "g", (N, H, dk), torch.float32, dev)
+    _check(beta, "beta", (N, H), q.dtype, dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (N, H, dv), q.dtype, dev)
+    desc = _abi.decode_desc(dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv,
+                            scale=0.0 if scale is None else float(scale), state=state.data_ptr(),
+                            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=g.data_ptr(),
+                            beta=beta.data_ptr(), o=out.data_ptr())
+    st = _abi.recurrent_decode_raw(desc, _stream(stream))
+    if st != _abi.KDA_OK:
+        raise _abi.KdaError(st, "kda_recurrent_decode")
+    return out
+
+
+def workspace_status(workspace: torch.Tensor, stream=None) -> int:
+    """Device status word of the last prefill that used `workspace`."""
+    return _abi.workspace_status(workspace.data_ptr(), _stream(stream))

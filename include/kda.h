@@ -1,0 +1,167 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * KDA is the gated delta rule with one decay per key channel ("per-channel-decay
+ * KDA"; page "spike(kimi-linear): chunk_kda prefill AOT port -- kernel set +
+ * pinned-config recipe", section Delivered).  Per (sequence, head) it keeps an
+ * fp32 state S with dk rows (key channels) and dv columns (value channels).
+ * One token with query q, key k, value v, log-decay g (natural log, one value
+ * per key channel) and write strength beta does
+ *
+ *     S <- (I - beta k k^T) Diag(exp(g)) S + beta k v^T
+ *     o  = scale * S^T q                 (the state after the update)
+ *
+ * The pages run this in two forms (page "Kimi-Linear: paged-incremental decode
+ * (prefill-once + carried-state decode)", squash commit): a chunked prefill
+ * over the prompt that returns the final state, and a recurrent decode that
+ * advances one token per call from the carried state and must read the state
+ * it is given.  Those are the two entry points below.
+ *
+ * Conventions (borrowed from the versioned C ABI on page "model(kimi_linear):
+ * ONE-SURFACE ROW 7 -- fold Kimi-Linear onto the shared paged runner",
+ * section Landed: a version constant, explicit descriptors, loud failure):
+ *   - Every descriptor starts with struct_size = sizeof(the struct); a
+ *     mismatch returns KDA_ERR_VERSION.  Fields documented "0 = default" may be
+ *     left zero.
+ *   - All pointers except those marked "host" are DEVICE pointers on the
+ *     current HIP device, owned by the caller.  The library allocates no device
+ *     memory and keeps no state between calls; calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; no call synchronises.
+ *   - Every argument check runs on the host before anything is enqueued; a
+ *     failed check returns a negative kda_status and enqueues nothing.  A
+ *     failed kernel launch returns KDA_ERR_HIP (kda_last_hip_error() has the
+ *     hipError_t).  NaN/Inf in the data propagate; data is not inspected.
+ *   - Tensors are dense row-major with the last index contiguous.  Alignment:
+ *     prefill q and k, and the decode state, 16 bytes (read as 16-byte
+ *     vectors); every other pointer, its element size.
+ *   - Supported: dk = dv = d in {32, 64, 128}; chunk in {16, 32, 64};
+ *     dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16 for q, k, v, beta and o.
+ *     g, h0, ht and the decode state are always fp32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  KDA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be,
+                               or too large                                    */
+  KDA_ERR_DTYPE = -3,       /* dtype is not one of kda_dtype                   */
+  KDA_ERR_UNSUPPORTED = -4, /* head dim or chunk size not supported           */
+  KDA_ERR_ALIGN = -5,       /* a pointer breaks its alignment rule (below)     */
+  KDA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
+  KDA_ERR_HIP = -7,         /* a HIP launch failed; see kda_last_hip_error()   */
+  KDA_ERR_VERSION = -8,     /* struct_size does not match this library        */
+  KDA_ERR_ALIAS = -9,       /* an output overlaps an input it may not overlap  */
+  KDA_ERR_SEQLENS = -10     /* cu_seqlens content invalid (reported through
+                               kda_workspace_status, never by a call's return) */
+} kda_status;
+
+typedef enum { KDA_DTYPE_F32 = 1, KDA_DTYPE_BF16 = 2 } kda_dtype;
+
+/* Chunked prefill over a packed batch of N sequences (T_total tokens).
+ *
+ * Computes, for every sequence n and head h, the recurrence above over the
+ * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 starting from h0[n,h] (zero when
+ * h0 is NULL), writes o for every token and the final state to ht[n,h].  The
+ * chunked form (cumulative decay, decayed K K^T, triangular solve, W/U, state
+ * recurrence, output; page "spike(kimi-linear): chunk_kda prefill AOT port",
+ * commit message) gives the same result as the token loop up to rounding, for
+ * any chunk size.
+ *
+ * Layouts: q, k, g [T_total, H, dk]; v, o [T_total, H, dv]; beta [T_total, H];
+ * h0, ht [N, H, dk, dv].  An empty sequence (length 0) writes no o and sets
+ * ht = h0 (zeros when h0 is NULL).
+ *
+ * cu_seqlens: device int32 [N + 1], cu[0] = 0, non-decreasing,
+ * cu[N] = t_total.  May be NULL only when n_seqs == 1.  Its contents are read
+ * on the device only: when they break these rules no o and no ht is written
+ * and kda_workspace_status() returns KDA_ERR_SEQLENS.
+ *
+ * Aliasing: ht may equal h0 (in-place carry).  o must not overlap any input.
+ * g is expected to be <= 0 (a decay); positive values are computed exactly as
+ * written but lose the bounds that keep the chunked factors in range. */
+typedef struct {
+  uint32_t struct_size;       /* sizeof(kda_prefill_desc)                       */
+  int32_t dtype;              /* kda_dtype of q, k, v, beta, o                  */
+  int32_t n_seqs;             /* N >= 1                                         */
+  int32_t n_heads;            /* H >= 1                                         */
+  int32_t dk, dv;             /* head dims; dk == dv in {32, 64, 128}           */
+  int32_t chunk;              /* 0 = 64; else 16, 32 or 64                      */
+  int64_t t_total;            /* packed tokens, >= 0                            */
+  float scale;                /* 0 = dk^-1/2                                    */
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const float* h0;            /* NULL = zero initial state                      */
+  const int32_t* cu_seqlens;  /* NULL allowed when n_seqs == 1                  */
+  void* o;
+  float* ht;                  /* NULL = final state not returned               */
+} kda_prefill_desc;
+
+/* One recurrent decode step for a batch of N sequences, one token each.
+ * state [N, H, dk, dv] fp32 is read and updated IN PLACE; q, k, g [N, H, dk];
+ * v, o [N, H, dv]; beta [N, H].  o must not overlap state or any input. */
+typedef struct {
+  uint32_t struct_size;       /* sizeof(kda_decode_desc)                        */
+  int32_t dtype;              /* kda_dtype of q, k, v, beta, o                  */
+  int32_t n_seqs;             /* N >= 0 (0 = nothing to do)                     */
+  int32_t n_heads;            /* H >= 1                                         */
+  int32_t dk, dv;             /* dk == dv in {32, 64, 128}                      */
+  float scale;                /* 0 = dk^-1/2                                    */
+  float* state;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  void* o;
+} kda_decode_desc;
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+/* Static text for a kda_status value ("unknown status" otherwise). */
+const char* kda_status_string(int status);
+
+/* hipError_t behind the last KDA_ERR_HIP returned on this thread (0 if none). */
+int kda_last_hip_error(void);
+
+/* Bytes of device workspace kda_chunk_prefill needs for this descriptor
+ * (depends on n_seqs, n_heads, dk, dv, chunk, dtype and t_total only).
+ * Returns 0 when the descriptor is invalid; *status (host, may be NULL)
+ * receives the kda_status of the check. */
+size_t kda_chunk_prefill_workspace_bytes(const kda_prefill_desc* d, int* status);
+
+/* Enqueue the chunked prefill on `stream`.  workspace: device buffer of at
+ * least kda_chunk_prefill_workspace_bytes(d) bytes, 256-byte aligned, owned by
+ * the caller, not shared with a concurrent call.  Returns a kda_status. */
+int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Device-side status of the last prefill that used `workspace`: KDA_OK or
+ * KDA_ERR_SEQLENS.  Copies one int to the host and synchronises `stream`.
+ * Returns KDA_ERR_HIP if the copy fails. */
+int kda_workspace_status(const void* workspace, void* stream);
+
+/* Enqueue one recurrent decode step on `stream`.  Returns a kda_status. */
+int kda_recurrent_decode(const kda_decode_desc* d, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

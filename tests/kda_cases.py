@@ -1,0 +1,50 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+oracle on the same (rounded) values, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}  # relative L2 bars for o and the final state
+
+
+def rel_l2(x, ref) -> float:
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / (n if n > 0 else 1.0))
+
+
+def to_dev(arr: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(dev)
+
+
+def to_host64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def dev_inputs(inp: synth.KdaInputs, dev="cuda") -> dict:
+    d = inp.dtype
+    return {
+        "q": to_dev(inp.q, d, dev), "k": to_dev(inp.k, d, dev), "v": to_dev(inp.v, d, dev),
+        "g": to_dev(inp.g, "f32", dev), "beta": to_dev(inp.beta, d, dev),
+        "h0": None if inp.h0 is None else to_dev(inp.h0, "f32", dev),
+        "cu_seqlens": torch.from_numpy(inp.cu_seqlens).to(dev),
+    }
+
+
+def oracle_prefill(inp: synth.KdaInputs):
+    f = inp.f64()
+    return oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"], f["cu_seqlens"],
+                          f["scale"])
+
+
+def say(msg: str):
+    print(msg, flush=True)
