@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""KDA forward benchmark on one MI355X.
+
+Workload (one timed step): the chunked prefill of one 32768-token sequence,
+32 heads, dk = dv = 128, 64-token chunks, bf16 q/k/v/beta/o, fp32 g, a nonzero
+fp32 initial state and fp32 final state -- the prefill-32k workload.  Beside it
+the recurrent decode leg: batch 64, 32 heads, d = 128, 256 successive
+one-token steps on a carried state produced by a chunked prefill of 1024
+tokens per sequence.
+
+Prints one JSON line.  `value` is prefill tokens/s with inputs resident in HBM.
+The roofline entry prices the prefill against HBM bandwidth with the
+algorithmic bytes of the pass (q, k, v, g, beta read once, o written once, h0
+read and hT written); per-kernel durations come from HIP events recorded on the
+launch stream around each of the three launches.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=32,d=128,T=32k) + decode steps/s; % of roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+# Algorithmic traffic per token, bf16 inputs, H = 32, d = 128: q, k, v (bf16),
+# g (fp32), beta (bf16) read once, o (bf16) written once.
+BYTES_PER_TOKEN = 3 * 8192 + 16384 + 64 + 8192  # 49,216
+STATE_BYTES = 32 * 128 * 128 * 4  # one sequence's h0 or hT
+# Algorithmic flops per (64-token chunk, head) of the chunked form.
+FLOPS_PER_CHUNK_HEAD = 9_041_236
+# Decode: state read + written per step, plus the step's q, k, v, g, beta, o.
+DECODE_STATE_BYTES = 64 * 32 * 128 * 128 * 4 * 2
+DECODE_TOKEN_BYTES = 64 * 32 * (128 * 2 * 3 + 128 * 4 + 2 + 128 * 2)
+DECODE_FLOPS = 64 * 32 * (7 * 128 * 128)
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = ["gated_delta_rule_55_amd/csrc/kda_prefill.hip",
+                  "gated_delta_rule_55_amd/csrc/kda_chunk_ops.h",
+                  "gated_delta_rule_55_amd/csrc/kda_decode.hip",
+                  "gated_delta_rule_55_amd/csrc/kda_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from committed counter runs, or None when absent or
+    taken on a different version of the kernel sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("source_hash") != kernel_source_hash():
+        return None
+    ent = data.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def to_dev(arr, torch):
+    import numpy as np
+
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(arr).cuda()
+
+
+def bench_prefill(args, torch, kda, synth):
+    log("generating the prefill-32k inputs (seeded numpy)")
+    inp = synth.make_config(2)
+    T, H, D = inp.T, inp.H, inp.dk
+    q, k, v = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v))
+    g, beta = to_dev(inp.g, torch), to_dev(inp.beta, torch)
+    h0 = to_dev(inp.h0, torch)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.prefill_workspace_bytes(T, H, D, 1, 64), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in ev:  # create the underlying events
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+
+    def run(events=None):
+        kda.chunk_prefill(q, k, v, g, beta, h0, None, scale=inp.scale, chunk=64, out=o, ht=ht,
+                          workspace=ws, events=events, plan=args.plan)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        run(ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    # events: before the chunk map, after it, after the next launch, after the
+    # last launch (the fused plan has a single launch after the chunk map)
+    stage = {"chunk_map": [], "fused_or_chunk_local": [], "state_scan": [], "prefill_call": []}
+    for row in ev:
+        stage["chunk_map"].append(row[0].elapsed_time(row[1]))
+        stage["fused_or_chunk_local"].append(row[1].elapsed_time(row[2]))
+        stage["state_scan"].append(row[2].elapsed_time(row[3]))
+        stage["prefill_call"].append(row[0].elapsed_time(row[3]))
+    avg = {kname: statistics.mean(vals) for kname, vals in stage.items()}
+    ms_per_step = total_ms / args.steps
+    return inp, ms_per_step, avg
+
+
+def bench_decode(args, torch, kda, synth):
+    log("generating the decode-64x256 inputs (seeded numpy)")
+    inp = synth.make_config(4)
+    N, L, P, S = 64, 1280, 1024, args.decode_steps
+    H, D = inp.H, inp.dk
+    dev = {name: to_dev(getattr(inp, name), torch) for name in ["q", "k", "v", "g", "beta"]}
+    view = lambda t: t.view(N, L, *t.shape[1:])  # noqa: E731
+    pre = {kk: view(t)[:, :P].reshape(N * P, *t.shape[1:]).contiguous() for kk, t in dev.items()}
+    dec = {kk: view(t)[:, P:P + S].transpose(0, 1).contiguous() for kk, t in dev.items()}
+    del dev
+    cu = torch.arange(0, N * P + 1, P, dtype=torch.int32, device="cuda")
+    _, state0 = kda.chunk_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, cu,
+                                  scale=inp.scale, chunk=64)
+    state = state0.clone()
+    out = torch.empty((S, N, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def steps():
+        for s in range(S):
+            kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
+                                 dec["beta"][s], scale=inp.scale, out=out[s])
+
+    state.copy_(state0)
+    steps()  # warm-up
+    times = []
+    for _ in range(args.decode_reps):
+        state.copy_(state0)  # restore, untimed
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        steps()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = statistics.median(times)
+    return inp, S, ms, dec
+
+
+def cpu_prefill_baseline(args, inp):
+    """The fp64 oracle (C, OpenMP over the 32 head chains) on the prefill-32k
+    inputs: the whole sequence, repeated until about --cpu-seconds of CPU time
+    has passed (at least once), reported as tokens/s."""
+    import oracle
+
+    f = inp.f64()
+    reps, total = 0, 0.0
+    while reps == 0 or total < args.cpu_seconds:
+        t0 = time.perf_counter()
+        oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"], None, f["scale"])
+        total += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * inp.T / total, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 token recurrence over all {inp.T} tokens x 32 heads of the "
+                      f"prefill-32k inputs (with h0), run {reps} times, {total:.1f} s in total"}
+
+
+def cpu_decode_baseline(inp, dec, n_steps=8):
+    import numpy as np
+
+    import oracle
+
+    N, H, D = 64, inp.H, inp.dk
+    st = np.zeros((N, H, D, D))
+    arrs = {kk: t[:n_steps].float().cpu().numpy().astype(np.float64) for kk, t in dec.items()}
+    t0 = time.perf_counter()
+    for s in range(n_steps):
+        _, st = oracle.decode(st, arrs["q"][s], arrs["k"][s], arrs["v"][s], arrs["g"][s],
+                              arrs["beta"][s], inp.scale)
+    dt = time.perf_counter() - t0
+    return {"value": n_steps / dt, "unit": "steps/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"{n_steps} fp64 decode steps at batch 64, H=32, d=128"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--plan", choices=["auto", "fused", "two_pass"], default="auto",
+                    help="prefill launch plan")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the KDA path shards by heads or sequences with no communication; "
+              "this build runs and reports a single GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gated_delta_rule_55_amd as kda
+    import synth
+
+    inp, ms_step, stage_ms = bench_prefill(args, torch, kda, synth)
+    T, H, D = inp.T, inp.H, inp.dk
+    tok_s = T / (ms_step / 1e3)
+    alg_bytes = T * BYTES_PER_TOKEN + 2 * STATE_BYTES
+    n_chunks = (T + 63) // 64
+    alg_flops = n_chunks * H * FLOPS_PER_CHUNK_HEAD
+    call_ms = stage_ms["prefill_call"]
+    achieved = alg_bytes / (call_ms / 1e3) / 1e9
+    traffic = measured_traffic("prefill")
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "scope": "whole prefill pass (chunk map + chunk-local + state scan), "
+                 f"{alg_bytes} algorithmic bytes per pass",
+        "mfma_frac": round(alg_flops / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels_ms": {kname: round(v, 4) for kname, v in stage_ms.items()},
+        "plan": args.plan,
+        "dominant_kernel": max(["fused_or_chunk_local", "state_scan"], key=lambda kn: stage_ms[kn]),
+    }
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill-32k: 1 sequence x 32768 tokens, H=32, dk=dv=128, "
+                               "chunk 64, bf16 q/k/v/beta/o, fp32 g, h0 ~ N(0, 0.02) fp32",
+                   "global_batch": 1, "seq_len": T, "heads": H, "head_dim": D, "chunk": 64,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    if not args.no_decode:
+        dinp, S, dms, dec = bench_decode(args, torch, kda, synth)
+        step_ms = dms / S
+        dbytes = DECODE_STATE_BYTES + DECODE_TOKEN_BYTES
+        dach = dbytes / (step_ms / 1e3) / 1e9
+        line["decode"] = {
+            "workload": "decode-64x256: batch 64, H=32, d=128, 256 steps on a state from a "
+                        "64 x 1024-token chunked prefill",
+            "steps_per_s": round(1e3 / step_ms, 1), "ms_per_step": round(step_ms, 5),
+            "tokens_per_s": round(64 * 1e3 / step_ms, 1),
+            "roofline": {"bound": "hbm", "achieved": round(dach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode"),
+                         "note": "the 134 MB state fits the 256 MB Infinity Cache"},
+        }
+        if not args.no_cpu:
+            log("timing the CPU oracle (decode)")
+            line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)
+        del dec
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_probe_bytes"] = 2 * n * 4
+    if not args.no_cpu:
+        log("timing the CPU oracle (prefill)")
+        line["cpu_baseline"] = cpu_prefill_baseline(args, inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

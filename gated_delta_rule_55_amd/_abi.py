@@ -20,6 +20,11 @@ KDA_ERR_HIP = -7
 KDA_ERR_VERSION = -8
 KDA_ERR_ALIAS = -9
 KDA_ERR_SEQLENS = -10
+KDA_ERR_SYNC = -11
+
+KDA_PLAN_AUTO = 0
+KDA_PLAN_FUSED = 1
+KDA_PLAN_TWO_PASS = 2
 
 KDA_DTYPE_F32 = 1
 KDA_DTYPE_BF16 = 2
@@ -34,6 +39,7 @@ class PrefillDesc(ctypes.Structure):
         ("dk", ctypes.c_int32),
         ("dv", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
+        ("plan", ctypes.c_int32),
         ("t_total", ctypes.c_int64),
         ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p),
@@ -98,6 +104,10 @@ def lib():
         L.kda_chunk_prefill.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
         L.kda_chunk_prefill.restype = ctypes.c_int
+        L.kda_chunk_prefill_timed.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.POINTER(ctypes.c_void_p)]
+        L.kda_chunk_prefill_timed.restype = ctypes.c_int
         L.kda_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kda_workspace_status.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.c_void_p]
@@ -138,6 +148,16 @@ def workspace_bytes(desc: PrefillDesc) -> int:
 
 def chunk_prefill_raw(desc: PrefillDesc, workspace: int, workspace_bytes: int, stream: int) -> int:
     return int(lib().kda_chunk_prefill(ctypes.byref(desc), workspace, workspace_bytes, stream))
+
+
+def chunk_prefill_timed_raw(desc: PrefillDesc, workspace: int, workspace_bytes: int,
+                            stream: int, events) -> int:
+    """events: four raw hipEvent_t handles (ints) or None."""
+    arr = None
+    if events is not None:
+        arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
+    return int(lib().kda_chunk_prefill_timed(ctypes.byref(desc), workspace, workspace_bytes,
+                                             stream, arr))
 
 
 def recurrent_decode_raw(desc: DecodeDesc, stream: int) -> int:

@@ -51,7 +51,10 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_supported(d->dtype == KDA_DTYPE_BF16, d->dk, chunk)) return KDA_ERR_UNSUPPORTED;
   if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
+  if (d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
+    return KDA_ERR_UNSUPPORTED;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
+  a->plan = d->plan;
   a->n_seqs = d->n_seqs;
   a->n_heads = d->n_heads;
   a->d = d->dk;
@@ -124,6 +127,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_VERSION: return "descriptor struct_size mismatch";
     case KDA_ERR_ALIAS: return "output overlaps an input";
     case KDA_ERR_SEQLENS: return "cu_seqlens content invalid";
+    case KDA_ERR_SYNC: return "fused prefill workgroups timed out waiting on each other";
     default: return "unknown status";
   }
 }
@@ -138,8 +142,8 @@ size_t kda_chunk_prefill_workspace_bytes(const kda_prefill_desc* d, int* status)
   return kda::prefill_workspace_bytes(a);
 }
 
-int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events) {
   kda::PrefillArgs a;
   int st = check_prefill(d, &a);
   if (st != KDA_OK) return st;
@@ -159,7 +163,13 @@ int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspa
                            range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0)};
   for (const Range& r : touched)
     if (overlap(rw, r)) return KDA_ERR_ALIAS;
-  return hip_status(kda::launch_prefill(a, workspace, (hipStream_t)stream));
+  return hip_status(kda::launch_prefill(a, workspace, (hipStream_t)stream,
+                                        reinterpret_cast<const hipEvent_t*>(events)));
+}
+
+int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return kda_chunk_prefill_timed(d, workspace, workspace_bytes, stream, nullptr);
 }
 
 int kda_workspace_status(const void* workspace, void* stream) {

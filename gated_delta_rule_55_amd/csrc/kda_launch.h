@@ -19,9 +19,14 @@ struct DecodeArgs {
   void* o;
 };
 
+// Launch plans (same values as kda_plan in include/kda.h).
+constexpr int KDA_PLAN_AUTO_ = 0;
+constexpr int KDA_PLAN_FUSED_ = 1;
+constexpr int KDA_PLAN_TWO_PASS_ = 2;
+
 struct PrefillArgs {
   bool bf16;
-  int n_seqs, n_heads, d, chunk;
+  int n_seqs, n_heads, d, chunk, plan;
   int64_t t_total;
   float scale;
   const void *q, *k, *v;
@@ -41,7 +46,10 @@ inline int64_t max_chunks(int64_t t_total, int n_seqs, int chunk) {
 // Whether the (dtype, head dim, chunk) instance is built.
 bool prefill_supported(bool bf16, int d, int chunk);
 size_t prefill_workspace_bytes(const PrefillArgs& a);
-hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
+// events: NULL, or four events recorded before the first launch and after
+// each of the three launches.
+hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream,
+                          const hipEvent_t* events);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // Offset of the device status word inside a prefill workspace.

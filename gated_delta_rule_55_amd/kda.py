@@ -36,14 +36,18 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+_PLANS = {"auto": _abi.KDA_PLAN_AUTO, "fused": _abi.KDA_PLAN_FUSED,
+          "two_pass": _abi.KDA_PLAN_TWO_PASS}
+
+
 def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
-                 ht=None) -> _abi.PrefillDesc:
+                 ht=None, plan="auto") -> _abi.PrefillDesc:
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
     return _abi.prefill_desc(
         dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv, chunk=int(chunk),
-        t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
+        plan=_PLANS[plan], t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
         v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
         o=_ptr(o), ht=_ptr(ht))
 
@@ -60,12 +64,16 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                   chunk: int = 64, out: Optional[torch.Tensor] = None,
                   ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  output_final_state: bool = True, stream=None
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  output_final_state: bool = True, stream=None, events=None,
+                  plan: str = "auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
     h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
     None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
-    `ht` may be h0 itself (in-place carry)."""
+    `ht` may be h0 itself (in-place carry).  `events`: four torch.cuda.Event
+    objects recorded before the first launch and after each of the three
+    launches (chunk map, chunk-local stage, state scan), for stage timing (the
+    fused plan has one launch after the chunk map; its time is reported as the
+    chunk-local stage).  `plan`: "auto", "fused" or "two_pass"."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("chunk_prefill runs on the GPU only")
@@ -91,12 +99,14 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif ht is not None:
         _check(ht, "ht", (N, H, dk, dv), torch.float32, dev)
-    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht)
+    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan)
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = _abi.chunk_prefill_raw(desc, workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream(stream))
+    handles = None if events is None else [e.cuda_event for e in events]
+    st = _abi.chunk_prefill_timed_raw(desc, workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream), handles)
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_chunk_prefill")
     return out, ht

@@ -64,11 +64,23 @@ typedef enum {
   KDA_ERR_HIP = -7,         /* a HIP launch failed; see kda_last_hip_error()   */
   KDA_ERR_VERSION = -8,     /* struct_size does not match this library        */
   KDA_ERR_ALIAS = -9,       /* an output overlaps an input it may not overlap  */
-  KDA_ERR_SEQLENS = -10     /* cu_seqlens content invalid (reported through
+  KDA_ERR_SEQLENS = -10,    /* cu_seqlens content invalid (reported through
                                kda_workspace_status, never by a call's return) */
+  KDA_ERR_SYNC = -11        /* the fused plan's workgroups stopped waiting on
+                               each other (reported through kda_workspace_status);
+                               o and ht are incomplete */
 } kda_status;
 
 typedef enum { KDA_DTYPE_F32 = 1, KDA_DTYPE_BF16 = 2 } kda_dtype;
+
+/* Launch plan of the chunked prefill.  FUSED runs the whole pass as one
+ * cooperative kernel whose chunk-local results stay on chip; TWO_PASS writes
+ * them to the workspace and reads them back (same results up to rounding
+ * order within a chunk step: both use the same arithmetic).  AUTO currently
+ * selects TWO_PASS, the faster of the two on MI355X as measured.  An explicit
+ * FUSED that cannot be honoured (the grid does not fit on the device at once)
+ * returns KDA_ERR_HIP. */
+typedef enum { KDA_PLAN_AUTO = 0, KDA_PLAN_FUSED = 1, KDA_PLAN_TWO_PASS = 2 } kda_plan;
 
 /* Chunked prefill over a packed batch of N sequences (T_total tokens).
  *
@@ -99,6 +111,7 @@ typedef struct {
   int32_t n_heads;            /* H >= 1                                         */
   int32_t dk, dv;             /* head dims; dk == dv in {32, 64, 128}           */
   int32_t chunk;              /* 0 = 64; else 16, 32 or 64                      */
+  int32_t plan;               /* kda_plan; 0 = auto                             */
   int64_t t_total;            /* packed tokens, >= 0                            */
   float scale;                /* 0 = dk^-1/2                                    */
   const void* q;
@@ -151,6 +164,13 @@ size_t kda_chunk_prefill_workspace_bytes(const kda_prefill_desc* d, int* status)
  * the caller, not shared with a concurrent call.  Returns a kda_status. */
 int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* kda_chunk_prefill that also records four caller-created hipEvent_t handles
+ * (passed as void*) on `stream`: events[0] before the first launch, then one
+ * after each of the three launches (chunk map, chunk-local stage, state scan),
+ * so the caller can time each stage.  events may be NULL (no recording). */
+int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* events);
 
 /* Device-side status of the last prefill that used `workspace`: KDA_OK or
  * KDA_ERR_SEQLENS.  Copies one int to the host and synchronises `stream`.

@@ -24,6 +24,7 @@ widened to fp64, so any measured difference is the GPU path's own.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Optional, Sequence
 
@@ -39,12 +40,17 @@ def _rng(seed: int, stream: str) -> np.random.Generator:
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (8 significant bits, ties to even) and return
     the bit patterns as uint16.  Values must lie in the normal bf16 range or be
-    zero (true for every distribution above)."""
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)
-    r = np.ldexp(np.rint(m * 256.0) / 256.0, e)  # exact fp64 value of the bf16
-    f = r.astype(np.float32)  # exact: at most 8 significant bits
-    return (f.view(np.uint32) >> 16).astype(np.uint16)
+    zero (true for every distribution above).
+
+    The rounding works on the fp64 bit pattern: the 45 low mantissa bits are
+    dropped with round-to-nearest-even (add 2^44 - 1 plus the lowest kept bit,
+    then clear them); the result is exact in fp32, whose top 16 bits are the
+    bf16."""
+    b = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).view(np.uint64)
+    keep = (b >> np.uint64(45)) & np.uint64(1)
+    r = (b + (np.uint64((1 << 44) - 1) + keep)) & ~np.uint64((1 << 45) - 1)
+    f = r.view(np.float64).astype(np.float32)  # exact: at most 8 significant bits
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -148,28 +154,43 @@ def make_inputs(
     cu = np.zeros(N + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
 
-    q = _l2norm(_rng(seed, "q").standard_normal((T, H, dk)))
-    k = _l2norm(_rng(seed, "k").standard_normal((T, H, dk)))
-    v = _rng(seed, "v").standard_normal((T, H, dv))
-    beta = 1.0 / (1.0 + np.exp(-_rng(seed, "beta").standard_normal((T, H))))
-    x = _rng(seed, "x").standard_normal((T, H, dk))
-    if gate == "softplus":
-        g = -_softplus(x)
-    elif gate == "kimi":
-        a = _rng(seed, "a").uniform(-3.0, 0.0, size=(H,))
-        b = _rng(seed, "b").normal(0.0, 0.5, size=(H, dk))
-        g = -np.exp(a)[None, :, None] * _softplus(x + b[None, :, :])
-    else:
+    # The independent streams are drawn on worker threads (numpy's generators
+    # release the GIL); each stream's values do not depend on the threading.
+    def draw_q():
+        return _store(_l2norm(_rng(seed, "q").standard_normal((T, H, dk))), dtype)
+
+    def draw_k():
+        return _store(_l2norm(_rng(seed, "k").standard_normal((T, H, dk))), dtype)
+
+    def draw_v():
+        return _store(_rng(seed, "v").standard_normal((T, H, dv)), dtype)
+
+    def draw_g():
+        x = _rng(seed, "x").standard_normal((T, H, dk))
+        if gate == "softplus":
+            g = -_softplus(x)
+        elif gate == "kimi":
+            a = _rng(seed, "a").uniform(-3.0, 0.0, size=(H,))
+            b = _rng(seed, "b").normal(0.0, 0.5, size=(H, dk))
+            g = -np.exp(a)[None, :, None] * _softplus(x + b[None, :, :])
+        else:
+            raise ValueError(f"unknown gate {gate!r}")
+        return np.ascontiguousarray(g.astype(np.float32))
+
+    if gate not in ("softplus", "kimi"):
         raise ValueError(f"unknown gate {gate!r}")
-    del x
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        futs = [pool.submit(f) for f in (draw_q, draw_k, draw_v, draw_g)]
+        q_s, k_s, v_s, g_s = (f.result() for f in futs)
+    beta = 1.0 / (1.0 + np.exp(-_rng(seed, "beta").standard_normal((T, H))))
     h0 = None
     if h0_std > 0.0:
         h0 = _rng(seed, "h0").normal(0.0, h0_std, size=(N, H, dk, dv)).astype(np.float32)
     return KdaInputs(
-        q=_store(q, dtype),
-        k=_store(k, dtype),
-        v=_store(v, dtype),
-        g=np.ascontiguousarray(g.astype(np.float32)),
+        q=q_s,
+        k=k_s,
+        v=v_s,
+        g=g_s,
         beta=_store(beta, dtype),
         h0=h0,
         cu_seqlens=cu,

@@ -1,0 +1,163 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/kda.h declares, and rejects bad descriptors before touching the GPU.
+No GPU is needed: every call here fails validation (or only sizes the
+workspace), so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The pointer checks below pass made-up device addresses that validation must
+# reject.  They run where no GPU is visible, so a validation bug can never turn
+# into a launch with those addresses.
+no_gpu_only = pytest.mark.skipif(_gpu_present(), reason="fake-pointer checks run without a GPU")
+
+
+@pytest.fixture(scope="module")
+def abi():
+    from gated_delta_rule_55_amd import _abi
+
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return _abi
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kda_[a-z_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(abi):
+    names = declared_functions()
+    assert "kda_chunk_prefill" in names and "kda_recurrent_decode" in names
+    lib = ctypes.CDLL(abi.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_version_and_strings(abi):
+    L = abi.lib()
+    assert L.kda_abi_version() == abi.KDA_ABI_VERSION
+    for st in range(0, -11, -1):
+        assert abi.status_string(st) != "unknown status"
+    assert abi.status_string(-99) == "unknown status"
+
+
+def test_struct_sizes_match_header(abi, tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text('#include <stdio.h>\n#include "kda.h"\n'
+                   'int main(void){printf("%zu %zu", sizeof(kda_prefill_desc),'
+                   ' sizeof(kda_decode_desc));return 0;}\n')
+    exe = tmp_path / "sz"
+    os.system(f"gcc -I{ROOT}/include {src} -o {exe}")
+    out = os.popen(str(exe)).read().split()
+    assert [int(x) for x in out] == [ctypes.sizeof(abi.PrefillDesc), ctypes.sizeof(abi.DecodeDesc)]
+
+
+def _valid_prefill(abi, **over):
+    kw = dict(dtype=abi.KDA_DTYPE_BF16, n_seqs=1, n_heads=2, dk=128, dv=128, chunk=64,
+              t_total=100, q=0x100000, k=0x200000, v=0x300000, g=0x400000, beta=0x500000,
+              o=0x600000)
+    kw.update(over)
+    return abi.prefill_desc(**kw)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=0), -3), (dict(dtype=3), -3), (dict(n_seqs=0), -2), (dict(n_heads=0), -2),
+    (dict(t_total=-1), -2), (dict(dk=96, dv=96), -4), (dict(dk=128, dv=64), -4),
+    (dict(chunk=48), -4), (dict(dtype=1, chunk=64), -4),
+])
+def test_workspace_query_validation(abi, over, status):
+    d = _valid_prefill(abi, **over)
+    st = ctypes.c_int(0)
+    n = abi.lib().kda_chunk_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(st))
+    assert st.value == status and n == 0
+
+
+def test_workspace_query_sizes(abi):
+    d = _valid_prefill(abi)
+    n = abi.workspace_bytes(d)
+    assert n > 0 and n % 256 == 0
+    d2 = _valid_prefill(abi, t_total=1000)
+    assert abi.workspace_bytes(d2) >= n
+    d3 = _valid_prefill(abi, struct_size=8)
+    st = ctypes.c_int(0)
+    abi.lib().kda_chunk_prefill_workspace_bytes(ctypes.byref(d3), ctypes.byref(st))
+    assert st.value == abi.KDA_ERR_VERSION
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(n_seqs=2), -1),   # cu_seqlens NULL, N > 1
+    (dict(q=0x100008), -5), (dict(g=0x400002), -5),
+    (dict(o=0x100000 + 64), -9),                                      # o overlaps q
+    (dict(h0=0x700000, ht=0x700000 + 16), -9),                        # ht partly overlaps h0
+])
+def test_prefill_rejects_bad_pointers(abi, over, status):
+    d = _valid_prefill(abi, **over)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == status
+
+
+@no_gpu_only
+def test_prefill_rejects_small_or_missing_workspace(abi):
+    d = _valid_prefill(abi)
+    need = abi.workspace_bytes(d)
+    assert abi.chunk_prefill_raw(d, 0, need, 0) == abi.KDA_ERR_WORKSPACE
+    assert abi.chunk_prefill_raw(d, 0x10000000, need - 1, 0) == abi.KDA_ERR_WORKSPACE
+    assert abi.chunk_prefill_raw(d, 0x10000000 + 16, need, 0) == abi.KDA_ERR_ALIGN
+    assert abi.chunk_prefill_raw(d, 0x100000 - 256, need, 0) == abi.KDA_ERR_ALIAS
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(struct_size=4), -8), (dict(dtype=9), -3), (dict(n_heads=0), -2), (dict(n_seqs=-1), -2),
+    (dict(dk=64, dv=128), -4), (dict(state=None), -1), (dict(state=0x100008), -5),
+    (dict(o=0x100000), -9),
+])
+def test_decode_validation(abi, over, status):
+    kw = dict(dtype=abi.KDA_DTYPE_BF16, n_seqs=2, n_heads=2, dk=64, dv=64, state=0x100000,
+              q=0x900000, k=0xa00000, v=0xb00000, g=0xc00000, beta=0xd00000, o=0xe00000)
+    kw.update(over)
+    d = abi.decode_desc(**kw)
+    if "struct_size" in over:
+        d.struct_size = over["struct_size"]
+    assert abi.recurrent_decode_raw(d, 0) == status
+
+
+@no_gpu_only
+def test_null_descriptors(abi):
+    L = abi.lib()
+    assert L.kda_chunk_prefill(None, None, 0, None) == abi.KDA_ERR_NULL
+    assert L.kda_recurrent_decode(None, None) == abi.KDA_ERR_NULL
+    assert L.kda_workspace_status(None, None) == abi.KDA_ERR_NULL
+
+
+@no_gpu_only
+def test_decode_zero_batch_is_noop(abi):
+    d = abi.decode_desc(dtype=abi.KDA_DTYPE_F32, n_seqs=0, n_heads=1, dk=32, dv=32)
+    assert abi.recurrent_decode_raw(d, 0) == abi.KDA_OK
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch):
+    from gated_delta_rule_55_amd import _abi
+
+    monkeypatch.setattr(_abi, "_LIB", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libkda.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.lib()
