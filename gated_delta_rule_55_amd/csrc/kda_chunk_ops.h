@@ -1,5 +1,5 @@
 // kda_chunk_ops.h -- device building blocks of the chunked KDA prefill:
-//   ChunkLocal  the chunk-local stage for one (chunk, head) by one 256-thread
+//   ChunkLocal  the chunk-local stage for one (chunk, head) by one 512-thread
 //               workgroup: cumulative decay, decayed Gram matrices, triangular
 //               solve, W/U and the chunk's output operators
 //   ScanStep    one step of the inter-chunk state recurrence with the output
@@ -40,6 +40,7 @@ __host__ __device__ constexpr size_t cmaxz(size_t a, size_t b) { return a > b ? 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLocalThreads = 512;  // threads of a chunk-local workgroup (8 waves)
 constexpr float kSpanMax = 64.0f;  // largest log2 diagonal factor taken on the factored path
 
 // Chunk table entry.
@@ -92,8 +93,14 @@ struct Geo {
   static constexpr size_t OFF_VBT = OFF_KBT + (size_t)D * TK_LD * sizeof(TIO);
   static constexpr size_t OFF_TB = OFF_VBT + (size_t)D * TK_LD * sizeof(TIO);
   static constexpr size_t OFF_AQ = OFF_TB + (size_t)C * TK_LD * sizeof(TIO);
+  static constexpr size_t OFF_VS = OFF_RN;  // raw v, row-major, until the scaled operands
   static constexpr size_t OFF_RHO = align_up(OFF_AQ + (size_t)C * TK_LD * sizeof(TIO), 16);
-  static constexpr size_t OFF_BETA = OFF_RHO + (size_t)(TT + 1) * D * 4;
+  // Per-channel factor vectors: 2^rho_a (TT), diagonal 2^(rho_a - rho_a+1) (TT),
+  // Kg 2^(rho_TT - rho_b+1) (TT), far pairs 2^(rho_a - rho_b+1), b <= a - 2.
+  static constexpr int NFAR = TT >= 3 ? (TT - 1) * (TT - 2) / 2 : 0;
+  static constexpr int NFAC = 3 * TT + NFAR;
+  static constexpr size_t OFF_FAC = OFF_RHO + (size_t)(TT + 1) * D * 4;
+  static constexpr size_t OFF_BETA = OFF_FAC + (size_t)NFAC * D * 4;
   static constexpr size_t OFF_FLAG = OFF_BETA + (size_t)C * 4;
   static constexpr size_t LOCAL_LDS = align_up(OFF_FLAG + 16, 16);
 
@@ -135,11 +142,13 @@ struct ChunkLocal {
   static constexpr int TT = Gm::TT, DT = Gm::DT, KBD = Gm::KBD, KCP = Gm::KCP, KBC = Gm::KBC;
   static constexpr int GS_LD = Gm::GS_LD, KS_LD = Gm::KS_LD, TK_LD = Gm::TK_LD,
                        AF_LD = Gm::AF_LD;
+  static constexpr int NT = kLocalThreads;          // threads of the workgroup
+  static constexpr int NW = NT / 64;                // waves
   static constexpr int EPV = 16 / sizeof(TIO);      // elements per 16-byte vector
   static constexpr int VPR = D / EPV;               // vectors per row of q, k, v
-  static constexpr int NV = (C * VPR + 255) / 256;  // vectors per thread per tensor
+  static constexpr int NV = (C * VPR + NT - 1) / NT;  // vectors per thread per tensor
   static constexpr int GPR = D / 4;                 // float4 per row of g
-  static constexpr int NG = (C * GPR + 255) / 256;  // float4 per thread of g
+  static constexpr int NG = (C * GPR + NT - 1) / NT;  // float4 per thread of g
 
   // The chunk's inputs as this thread loads them (rows beyond L are zero).
   struct Inputs {
@@ -163,7 +172,7 @@ struct ChunkLocal {
     in.len = L;
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      const int x = tid + 256 * m;
+      const int x = tid + NT * m;
       const int r = x / VPR, cv = x % VPR;
       in.k[m] = in.q[m] = in.v[m] = uint4{0, 0, 0, 0};
       if (x < C * VPR && r < L) {
@@ -175,7 +184,7 @@ struct ChunkLocal {
     }
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
-      const int x = tid + 256 * m;
+      const int x = tid + NT * m;
       const int r = x / GPR, cv = x % GPR;
       in.g[m] = zero4();
       if (x < C * GPR && r < L)
@@ -215,8 +224,31 @@ struct ChunkLocal {
     }
   }
 
-  // The whole stage.  Six workgroup barriers; all 256 threads must call it.
-  // `in` must have been filled by prefetch() for this (chunk, head).
+  static __device__ __forceinline__ int fac_sa(int a) { return a; }
+  static __device__ __forceinline__ int fac_diag(int a) { return TT + a; }
+  static __device__ __forceinline__ int fac_kg(int b) { return 2 * TT + b; }
+  static __device__ __forceinline__ int fac_far(int a, int b) {
+    return 3 * TT + (a - 2) * (a - 1) / 2 + b;
+  }
+
+  // Scale the 8 values of a bf16 / fp32 fragment by 8 per-channel factors.
+  static __device__ __forceinline__ FragT scale8(FragT f, const float* fac) {
+    const f32x4 f0 = *reinterpret_cast<const f32x4*>(fac);
+    const f32x4 f1 = *reinterpret_cast<const f32x4*>(fac + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = from_f32<TIO>(to_f32(f[e]) * f0[e]);
+      f[4 + e] = from_f32<TIO>(to_f32(f[4 + e]) * f1[e]);
+    }
+    return f;
+  }
+
+  // Number of workgroup barriers run() executes (every thread must call it).
+  static constexpr int NBAR = 5 + (TT - 1);
+
+  // The whole stage (every thread of the workgroup must call it).  `in` must
+  // have been filled by prefetch() for this
+  // (chunk, head); run() never waits on global memory otherwise.
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
                              ChunkOut<TIO> out, const TIO* __restrict__ q,
                              const TIO* __restrict__ k, const float* __restrict__ g, int n_heads,
@@ -228,11 +260,13 @@ struct ChunkLocal {
     TIO* Lk = reinterpret_cast<TIO*>(lds + Gm::OFF_LK);
     TIO* Lq = reinterpret_cast<TIO*>(lds + Gm::OFF_LQ);
     TIO* Rn = reinterpret_cast<TIO*>(lds + Gm::OFF_RN);
+    TIO* Vs = reinterpret_cast<TIO*>(lds + Gm::OFF_VS);
     TIO* KBt = reinterpret_cast<TIO*>(lds + Gm::OFF_KBT);
     TIO* VBt = reinterpret_cast<TIO*>(lds + Gm::OFF_VBT);
     TIO* Tb = reinterpret_cast<TIO*>(lds + Gm::OFF_TB);
     TIO* Aq = reinterpret_cast<TIO*>(lds + Gm::OFF_AQ);
     float* rho = reinterpret_cast<float*>(lds + Gm::OFF_RHO);  // [TT + 1][D]
+    float* fac = reinterpret_cast<float*>(lds + Gm::OFF_FAC);  // [NFAC][D]
     float* s_beta = reinterpret_cast<float*>(lds + Gm::OFF_BETA);
     int* s_flag = reinterpret_cast<int*>(lds + Gm::OFF_FLAG);
 
@@ -242,20 +276,25 @@ struct ChunkLocal {
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     const TIO zero_t = from_f32<TIO>(0.f);
+    // (8 rows x 1 channel) groups of the elementwise passes: lanes run along
+    // channels, so scalar LDS accesses of a row are conflict-free and the
+    // eight tokens of a group leave as one 16-byte transposed store.
+    constexpr int NGRP = (C / 8) * D / NT > 0 ? (C / 8) * D / NT : 1;
 
-    // ---- phase 0: stage k, q, g (base 2) and beta; clear padded operands ----
+    // ---- phase 0: stage k, q, v, g (base 2) and beta; clear padding --------
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      const int x = tid + 256 * m;
+      const int x = tid + NT * m;
       if (x < C * VPR) {
         const int r = x / VPR, cv = x % VPR;
         reinterpret_cast<uint4*>(Lk + r * KS_LD)[cv] = in.k[m];
         reinterpret_cast<uint4*>(Lq + r * KS_LD)[cv] = in.q[m];
+        reinterpret_cast<uint4*>(Vs + r * KS_LD)[cv] = in.v[m];
       }
     }
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
-      const int x = tid + 256 * m;
+      const int x = tid + NT * m;
       if (x < C * GPR) {
         const int r = x / GPR, cv = x % GPR;
         *reinterpret_cast<f32x4*>(Gs + r * GS_LD + 4 * cv) = in.g[m] * kLog2e;
@@ -263,100 +302,116 @@ struct ChunkLocal {
     }
     if (tid < C) s_beta[tid] = in.beta;
     if (tid == 0) *s_flag = 0;
-    for (int x = tid; x < C * TK_LD; x += 256) {
-      Tb[x] = zero_t;
-      Aq[x] = zero_t;
-    }
-    if constexpr (KCP != C)
-      for (int x = tid; x < D * TK_LD; x += 256) {
-        KBt[x] = zero_t;
-        VBt[x] = zero_t;
+    {
+      constexpr int NZ = C * TK_LD * (int)sizeof(TIO) / 16;  // uint4 per array
+      for (int x = tid; x < NZ; x += NT) {
+        reinterpret_cast<uint4*>(Tb)[x] = uint4{0, 0, 0, 0};
+        reinterpret_cast<uint4*>(Aq)[x] = uint4{0, 0, 0, 0};
       }
+      if constexpr (KCP != C) {
+        constexpr int NZB = D * TK_LD * (int)sizeof(TIO) / 16;
+        for (int x = tid; x < NZB; x += NT) {
+          reinterpret_cast<uint4*>(KBt)[x] = uint4{0, 0, 0, 0};
+          reinterpret_cast<uint4*>(VBt)[x] = uint4{0, 0, 0, 0};
+        }
+      }
+    }
     __syncthreads();
 
-    // ---- phase 1: cumulative sum over tokens; beta v transposed ----------
+    // ---- phase 1: cumulative sum over tokens; reference points; beta v ----
     {
-      // LPC lanes of one wave share a channel, each scanning C / LPC tokens;
-      // the segment totals are combined with lane shuffles.
-      constexpr int CPW = D / 4;         // channels per wave
-      constexpr int LPC = 64 / CPW;      // lanes per channel
-      constexpr int SEG = C / LPC;       // tokens per lane
+      // LPC lanes of one wave share a channel, each scanning SEG tokens held
+      // in registers; segment totals are combined with lane shuffles.
+      constexpr int CPW = D / NW;    // channels per wave
+      constexpr int LPC = 64 / CPW;  // lanes per channel
+      constexpr int SEG = C / LPC;   // tokens per lane
       const int c = wave * CPW + lane % CPW;
       const int seg = lane / CPW;
-      float run = 0.f;
+      float gv[SEG];
 #pragma unroll
-      for (int j = 0; j < SEG; ++j) {
-        float* p = Gs + (seg * SEG + j) * GS_LD + c;
-        run += *p;
-        *p = run;
-      }
+      for (int j = 0; j < SEG; ++j) gv[j] = Gs[(seg * SEG + j) * GS_LD + c];
+#pragma unroll
+      for (int j = 1; j < SEG; ++j) gv[j] += gv[j - 1];
       float before = 0.f;  // sum of the earlier segments' totals
 #pragma unroll
       for (int s2 = 0; s2 < LPC - 1; ++s2) {
-        const float tot = __shfl(run, (lane % CPW) + s2 * CPW, 64);
+        const float tot = __shfl(gv[SEG - 1], (lane % CPW) + s2 * CPW, 64);
         if (s2 < seg) before += tot;
       }
-      if (seg > 0) {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) Gs[(seg * SEG + j) * GS_LD + c] += before;
+      for (int j = 0; j < SEG; ++j) {
+        const int r = seg * SEG + j;
+        const float G = gv[j] + before;
+        Gs[r * GS_LD + c] = G;
+        if ((r & 15) == 0) rho[(r >> 4) * D + c] = G;
+        if (r == C - 1) rho[TT * D + c] = G;
       }
     }
 #pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      const int x = tid + 256 * m;
-      if (x < C * VPR) {
-        const int r = x / VPR, cv = x % VPR;
-        const float b = s_beta[r];
-        const TIO* ve = reinterpret_cast<const TIO*>(&in.v[m]);
+    for (int m = 0; m < NGRP; ++m) {
+      const int grp = tid + NT * m;
+      const int c = grp % D, r0 = 8 * (grp / D);
+      if (r0 < C) {
+        typename Frag<TIO>::type vb;
 #pragma unroll
-        for (int e = 0; e < EPV; ++e)
-          VBt[(cv * EPV + e) * TK_LD + r] = from_f32<TIO>(b * to_f32(ve[e]));
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 2: reference points, scaled operands ----------------------
-    {
-      constexpr int RPS = 256 / D;  // row stride of one thread
-      const int c = tid % D;
-      const int r0 = tid / D;
-      float rh[TT + 1], sa[TT];
-#pragma unroll
-      for (int a = 0; a < TT; ++a) rh[a] = Gs[(16 * a) * GS_LD + c];
-      rh[TT] = Gs[(C - 1) * GS_LD + c];
-#pragma unroll
-      for (int a = 0; a < TT; ++a) sa[a] = fast_exp2(rh[a]);
-      if (r0 == 0) {
-#pragma unroll
-        for (int a = 0; a <= TT; ++a) rho[a * D + c] = rh[a];
-        int big = 0;
-#pragma unroll
-        for (int a = 0; a < TT; ++a)
-          if (rh[a] - rh[a + 1] > kSpanMax) big |= 1 << a;
-        if (big) atomicOr(s_flag, big);
-      }
-#pragma unroll 4
-      for (int r = r0; r < C; r += RPS) {
-        const int a = r >> 4;
-        const float gr = Gs[r * GS_LD + c];
-        const float el = fast_exp2(gr - rh[a]);
-        const float er = fast_exp2(rh[a + 1] - gr);
-        const float kv = to_f32(Lk[r * KS_LD + c]);
-        const float qv = to_f32(Lq[r * KS_LD + c]);
-        const float lk = kv * el;
-        Lk[r * KS_LD + c] = from_f32<TIO>(lk);
-        Lq[r * KS_LD + c] = from_f32<TIO>(qv * el);
-        Rn[r * KS_LD + c] = from_f32<TIO>(kv * er);
-        KBt[c * TK_LD + r] = from_f32<TIO>(s_beta[r] * lk * sa[a]);
+        for (int e = 0; e < 8; ++e)
+          vb[e] = from_f32<TIO>(s_beta[r0 + e] * to_f32(Vs[(r0 + e) * KS_LD + c]));
+        store_frag8(VBt + c * TK_LD + r0, vb);
       }
     }
     __syncthreads();
 
-    // ---- phase 3: decayed Gram tiles; Kg fragments; Gam ------------------
+    // ---- phase 2: scaled operands Lk, Lq, Rn, beta k 2^G (transposed) ------
+    //      and the per-channel factor vectors
+#pragma unroll
+    for (int m = 0; m < NGRP; ++m) {
+      const int grp = tid + NT * m;
+      const int c = grp % D, r0 = 8 * (grp / D);
+      if (r0 < C) {
+        const int a = r0 >> 4;
+        const float ra = rho[a * D + c], rb = rho[(a + 1) * D + c];
+        const float sa = fast_exp2(ra);
+        typename Frag<TIO>::type kb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = r0 + e;
+          const float G = Gs[r * GS_LD + c];
+          const float el = fast_exp2(G - ra);
+          const float er = fast_exp2(rb - G);
+          const float kv = to_f32(Lk[r * KS_LD + c]);
+          const float qv = to_f32(Lq[r * KS_LD + c]);
+          const float lk = kv * el;
+          Lk[r * KS_LD + c] = from_f32<TIO>(lk);
+          Lq[r * KS_LD + c] = from_f32<TIO>(qv * el);
+          Rn[r * KS_LD + c] = from_f32<TIO>(kv * er);
+          kb[e] = from_f32<TIO>(s_beta[r] * lk * sa);
+        }
+        store_frag8(KBt + c * TK_LD + r0, kb);
+      }
+    }
+    for (int c = tid; c < D; c += NT) {
+      float rh[TT + 1];
+#pragma unroll
+      for (int a = 0; a <= TT; ++a) rh[a] = rho[a * D + c];
+      int big = 0;
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        fac[fac_sa(a) * D + c] = fast_exp2(rh[a]);
+        fac[fac_diag(a) * D + c] = fast_exp2(rh[a] - rh[a + 1]);
+        fac[fac_kg(a) * D + c] = fast_exp2(rh[TT] - rh[a + 1]);
+        if (rh[a] - rh[a + 1] > kSpanMax) big |= 1 << a;
+#pragma unroll
+        for (int b = 0; b + 2 <= a; ++b) fac[fac_far(a, b) * D + c] = fast_exp2(rh[a] - rh[b + 1]);
+      }
+      if (big) atomicOr(s_flag, big);
+    }
+    __syncthreads();
+
+    // ---- phase 3: decayed Gram tiles; Kg fragments; Gam -------------------
     {
       constexpr int NPAIR = TT * (TT + 1) / 2;
       const int flag = *s_flag;
-      for (int p = wave; p < NPAIR; p += 4) {
+      for (int p = wave; p < NPAIR; p += NW) {
         int a = 0, b = p;
         while (b > a) {
           b -= a + 1;
@@ -369,20 +424,17 @@ struct ChunkLocal {
           const TIO* lkr = Lk + (16 * a + l16) * KS_LD;
           const TIO* lqr = Lq + (16 * a + l16) * KS_LD;
           const TIO* rnr = Rn + (16 * b + l16) * KS_LD;
-          const bool scaled = (b != a - 1);  // adjacent blocks need no factor
+          // adjacent blocks need no factor; the rest one per channel
+          const float* fv = nullptr;
+          if (a == b) fv = fac + fac_diag(a) * D;
+          else if (b + 2 <= a) fv = fac + fac_far(a, b) * D;
 #pragma unroll
           for (int s = 0; s < KBD; ++s) {
             const int c0 = 32 * s + 8 * lg;
             const FragT fk = load_frag8<TIO>(lkr + c0);
             const FragT fq = load_frag8<TIO>(lqr + c0);
             FragT fr = load_frag8<TIO>(rnr + c0);
-            if (scaled) {
-              const float* ra = rho + a * D + c0;
-              const float* rb = rho + (b + 1) * D + c0;
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                fr[e] = from_f32<TIO>(to_f32(fr[e]) * fast_exp2(ra[e] - rb[e]));
-            }
+            if (fv) fr = scale8(fr, fv + c0);
             akk = mma32(fk, fr, akk);
             aqk = mma32(fq, fr, aqk);
           }
@@ -398,7 +450,7 @@ struct ChunkLocal {
       }
       // Kg^T fragments in kperm token order: element (kt, ts, lane, e) =
       // Kg[32ts + kperm(lg, e)][16kt + l16], Kg = Rn * 2^(rho_TT - rho_{blk+1}).
-      for (int slot = tid; slot < DT * KBC * 64; slot += 256) {
+      for (int slot = tid; slot < DT * KBC * 64; slot += NT) {
         const int ln = slot & 63;
         const int kt = (slot >> 6) / KBC, ts = (slot >> 6) % KBC;
         const int c = 16 * kt + (ln & 15);
@@ -407,151 +459,137 @@ struct ChunkLocal {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int blk = 2 * ts + hh;  // 16-token block of these four tokens
-          float fac = 0.f;
-          if (blk < TT) fac = fast_exp2(rho[TT * D + c] - rho[(blk + 1) * D + c]);
+          const float fk = (blk < TT) ? fac[fac_kg(blk < TT ? blk : 0) * D + c] : 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int tok = 16 * blk + 4 * g4 + e;
-            const float val = (blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fac : 0.f;
-            f[4 * hh + e] = from_f32<TIO>(val);
+            f[4 * hh + e] = from_f32<TIO>((blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fk : 0.f);
           }
         }
-        *reinterpret_cast<FragT*>(out.k + (size_t)slot * 8) = f;
+        store_frag8(out.k + (size_t)slot * 8, f);
       }
-      for (int c = tid; c < D; c += 256) out.gam[c] = fast_exp2(rho[TT * D + c]);
+      for (int c = tid; c < D; c += NT) out.gam[c] = fast_exp2(rho[TT * D + c]);
     }
     __syncthreads();
 
-    // ---- phase 4: T = (I + A)^-1 by one wave -------------------------------
-    if (wave == 0) {
-      // diagonal 16x16 blocks by forward substitution: lane (block lg, column l16)
-      if (lg < TT) {
-        const int a = lg, j = l16;
-        float x[16];
+    // ---- phase 4: T = (I + A)^-1 ------------------------------------------
+    // Diagonal 16x16 blocks by forward substitution in wave 0 (lane = block
+    // lg, column l16); then the off-diagonal blocks one band at a time, one
+    // wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb  (fp32 MFMA).
+    if (wave == 0 && lg < TT) {
+      const int a = lg, j = l16;
+      float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float acc = (r == j) ? 1.f : 0.f;
-          const float* Ar = As + (16 * a + r) * AF_LD + 16 * a;
+      for (int r = 0; r < 16; ++r) {
+        const float* Ar = As + (16 * a + r) * AF_LD + 16 * a;
+        float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-          for (int i = 0; i < r; ++i) acc -= Ar[i] * x[i];
-          x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          Ts[(16 * a + r) * AF_LD + 16 * a + j] = x[r];
-          Tb[(16 * a + r) * TK_LD + 16 * a + j] = from_f32<TIO>(x[r]);
-        }
+        for (int i = 0; i < r; ++i) acc -= Ar[i] * x[i];
+        x[r] = acc;
       }
-      // off-diagonal blocks band by band: T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
 #pragma unroll
-      for (int d = 1; d < TT; ++d) {
-        wave_sync();
-        for (int a = d; a < TT; ++a) {
-          const int b = a - d;
-          f32x4 pacc = zero4();
-          for (int cc = b; cc < a; ++cc) {
-            float fa[4], fb[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              fa[m] = As[(16 * a + l16) * AF_LD + 16 * cc + 4 * m + lg];
-              fb[m] = Ts[(16 * cc + 4 * m + lg) * AF_LD + 16 * b + l16];
-            }
-            pacc = mma16_f32(fa, fb, pacc);
-          }
-          float ta[4], pb[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            ta[m] = Ts[(16 * a + l16) * AF_LD + 16 * a + 4 * lg + m];
-            pb[m] = pacc[m];
-          }
-          const f32x4 tab = mma16_f32(ta, pb, zero4());
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int rr = 16 * a + 4 * lg + m;
-            Ts[rr * AF_LD + 16 * b + l16] = -tab[m];
-            Tb[rr * TK_LD + 16 * b + l16] = from_f32<TIO>(-tab[m]);
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        Ts[(16 * a + r) * AF_LD + 16 * a + j] = x[r];
+        Tb[(16 * a + r) * TK_LD + 16 * a + j] = from_f32<TIO>(x[r]);
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int d = 1; d < TT; ++d) {
+      const int a = d + wave;
+      if (a < TT) {
+        const int b = a - d;
+        f32x4 pacc = zero4();
+        for (int cc = b; cc < a; ++cc) {
+          float fa[4], fb[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            fa[m] = As[(16 * a + l16) * AF_LD + 16 * cc + 4 * m + lg];
+            fb[m] = Ts[(16 * cc + 4 * m + lg) * AF_LD + 16 * b + l16];
+          }
+          pacc = mma16_f32(fa, fb, pacc);
+        }
+        float ta[4], pb[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          ta[m] = Ts[(16 * a + l16) * AF_LD + 16 * a + 4 * lg + m];
+          pb[m] = pacc[m];
+        }
+        const f32x4 tab = mma16_f32(ta, pb, zero4());
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int rr = 16 * a + 4 * lg + m;
+          Ts[rr * AF_LD + 16 * b + l16] = -tab[m];
+          Tb[rr * TK_LD + 16 * b + l16] = from_f32<TIO>(-tab[m]);
+        }
+      }
+      __syncthreads();
+    }
 
     // ---- phase 5: W^T, U, Q'^T, Ol -> outputs -------------------------------
-    // Wave w owns channel slices kb = w, w + 4, ... (tiles 2kb, 2kb + 1) of
-    // W^T and Q'^T and the same value-column tiles of U and Ol.
-    constexpr int MW = (KBD + 3) / 4;
+    // Wave w owns channel tiles ct = w, w + NW, ... of W^T and Q'^T and the
+    // same value-column tiles of U and Ol.
 #pragma unroll
-    for (int m = 0; m < MW; ++m) {
-      const int kb = wave + 4 * m;
-      if (kb < KBD) {
-        f32x4 ureg[2][TT];
+    for (int ct = wave; ct < DT; ct += NW) {
+      const int kb = ct >> 1, hh = ct & 1;
+      f32x4 ureg[TT];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int ct = 2 * kb + hh;
+      for (int t = 0; t < TT; ++t) {
+        f32x4 wacc = zero4(), uacc = zero4();
 #pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            f32x4 wacc = zero4(), uacc = zero4();
-#pragma unroll
-            for (int s = 0; s <= t / 2; ++s) {
-              const FragT fk = load_frag8<TIO>(KBt + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
-              const FragT ft = load_frag8<TIO>(Tb + (16 * t + l16) * TK_LD + 32 * s + 8 * lg);
-              const FragT fv = load_frag8<TIO>(VBt + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
-              wacc = mma32(fk, ft, wacc);  // W^T[16ct + 4lg + j][16t + l16]
-              uacc = mma32(ft, fv, uacc);  // U[16t + 4lg + j][16ct + l16]
-            }
-            ureg[hh][t] = uacc;
-            TIO* wout = out.w + ((size_t)(t * KBD + kb) * 64 + lane) * 8 + 4 * hh;
-            TIO* uout = out.u + ((size_t)(t * DT + ct) * 64 + lane) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const TIO wv = from_f32<TIO>(wacc[j]);
-              wout[j] = wv;
-              WT[(16 * ct + 4 * lg + j) * TK_LD + 16 * t + l16] = wv;
-              uout[j] = from_f32<TIO>(uacc[j]);
-            }
-          }
+        for (int s = 0; s <= t / 2; ++s) {
+          const FragT fk = load_frag8<TIO>(KBt + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
+          const FragT ft = load_frag8<TIO>(Tb + (16 * t + l16) * TK_LD + 32 * s + 8 * lg);
+          const FragT fv = load_frag8<TIO>(VBt + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
+          wacc = mma32(fk, ft, wacc);  // W^T[16ct + 4lg + j][16t + l16]
+          uacc = mma32(ft, fv, uacc);  // U[16t + 4lg + j][16ct + l16]
         }
-        if constexpr (KCP != C) {
+        ureg[t] = uacc;
+        TIO* wout = out.w + ((size_t)(t * KBD + kb) * 64 + lane) * 8 + 4 * hh;
+        TIO* uout = out.u + ((size_t)(t * DT + ct) * 64 + lane) * 4;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            for (int x = lane; x < 16 * (KCP - C); x += 64)
-              WT[(32 * kb + 16 * hh + x / (KCP - C)) * TK_LD + C + x % (KCP - C)] = zero_t;
+        for (int j = 0; j < 4; ++j) {
+          const TIO wv = from_f32<TIO>(wacc[j]);
+          wout[j] = wv;
+          WT[(16 * ct + 4 * lg + j) * TK_LD + 16 * t + l16] = wv;
+          uout[j] = from_f32<TIO>(uacc[j]);
         }
-        wave_sync();  // this wave's W^T rows are complete
+      }
+      if constexpr (KCP != C) {
+        for (int x = lane; x < 16 * (KCP - C); x += 64)
+          WT[(16 * ct + x / (KCP - C)) * TK_LD + C + x % (KCP - C)] = zero_t;
+      }
+      wave_sync();  // this wave's W^T rows are complete
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int ct = 2 * kb + hh;
+      for (int t = 0; t < TT; ++t) {
+        f32x4 acc = zero4();
 #pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s <= t / 2; ++s) {
-              const FragT fw = load_frag8<TIO>(WT + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
-              const FragT fa = load_frag8<TIO>(Aq + (16 * t + l16) * TK_LD + 32 * s + 8 * lg);
-              acc = mma32(fw, fa, acc);  // (Aqk W)^T[16ct + 4lg + j][16t + l16]
-            }
-            const int r = 16 * t + l16;
-            const int a = r >> 4;
-            TIO* qout = out.q + ((size_t)(t * KBD + kb) * 64 + lane) * 8 + 4 * hh;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int c = 16 * ct + 4 * lg + j;
-              const float qg = to_f32(Lq[r * KS_LD + c]) * fast_exp2(rho[a * D + c]);
-              qout[j] = from_f32<TIO>(scale * (qg - acc[j]));
-            }
-            f32x4 oacc = zero4();
-#pragma unroll
-            for (int s = 0; s <= t / 2; ++s) {
-              const FragT fa = load_frag_perm<TIO>(Aq + (16 * t + l16) * TK_LD + 32 * s, lg);
-              f32x4 u1 = zero4();
-              if (2 * s + 1 < TT) u1 = ureg[hh][2 * s + 1 < TT ? 2 * s + 1 : TT - 1];
-              oacc = mma32(fa, frag_from_d<TIO>(ureg[hh][2 * s], u1), oacc);
-            }
-            TIO* oout = out.o + ((size_t)(t * DT + ct) * 64 + lane) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) oout[j] = from_f32<TIO>(scale * oacc[j]);
-          }
+        for (int s = 0; s <= t / 2; ++s) {
+          const FragT fw = load_frag8<TIO>(WT + (16 * ct + l16) * TK_LD + 32 * s + 8 * lg);
+          const FragT fa = load_frag8<TIO>(Aq + (16 * t + l16) * TK_LD + 32 * s + 8 * lg);
+          acc = mma32(fw, fa, acc);  // (Aqk W)^T[16ct + 4lg + j][16t + l16]
         }
+        const int r = 16 * t + l16;
+        const int a = r >> 4;
+        TIO* qout = out.q + ((size_t)(t * KBD + kb) * 64 + lane) * 8 + 4 * hh;
+        const f32x4 qr = *reinterpret_cast<const f32x4*>(fac + fac_sa(a) * D + 16 * ct + 4 * lg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 16 * ct + 4 * lg + j;
+          const float qg = to_f32(Lq[r * KS_LD + c]) * qr[j];
+          qout[j] = from_f32<TIO>(scale * (qg - acc[j]));
+        }
+        f32x4 oacc = zero4();
+#pragma unroll
+        for (int s = 0; s <= t / 2; ++s) {
+          const FragT fa = load_frag_perm<TIO>(Aq + (16 * t + l16) * TK_LD + 32 * s, lg);
+          f32x4 u1 = zero4();
+          if (2 * s + 1 < TT) u1 = ureg[2 * s + 1 < TT ? 2 * s + 1 : TT - 1];
+          oacc = mma32(fa, frag_from_d<TIO>(ureg[2 * s], u1), oacc);
+        }
+        TIO* oout = out.o + ((size_t)(t * DT + ct) * 64 + lane) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) oout[j] = from_f32<TIO>(scale * oacc[j]);
       }
     }
   }
@@ -574,13 +612,16 @@ struct ScanStep {
     FragT w[TT], q[TT], k[2][KBC];
     TIO u[NOWN][4], ol[NOWN][4];
     f32x4 gam[2];
+    int start, len;  // the chunk's token range (set by the caller)
   };
 
+  // ALL: every wave of the workgroup holds a dk slice.
+  template <bool ALL>
   static __device__ __forceinline__ void load(Ops& op, const ChunkOut<TIO>& in, int jb) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int lg = lane >> 4;
-    if (w >= KBD) return;  // waves past the dk slices hold no state
+    if (!ALL && w >= KBD) return;  // waves past the dk slices hold no state
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       op.w[t] = load_frag8<TIO>(in.w + ((size_t)(t * KBD + w) * 64 + lane) * 8);
@@ -593,15 +634,14 @@ struct ScanStep {
         op.k[m][kc] = load_frag8<TIO>(in.k + ((size_t)((2 * w + m) * KBC + kc) * 64 + lane) * 8);
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
-      const int t = w + KBD * i;
-      if (t < TT) {
-        const TIO* Uc = in.u + ((size_t)(t * DT + jb) * 64 + lane) * 4;
-        const TIO* Oc = in.o + ((size_t)(t * DT + jb) * 64 + lane) * 4;
+      const int t0 = w + KBD * i;
+      const int t = t0 < TT ? t0 : TT - 1;  // tiles past the chunk are loaded, then unused
+      const TIO* Uc = in.u + ((size_t)(t * DT + jb) * 64 + lane) * 4;
+      const TIO* Oc = in.o + ((size_t)(t * DT + jb) * 64 + lane) * 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          op.u[i][j] = Uc[j];
-          op.ol[i][j] = Oc[j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        op.u[i][j] = Uc[j];
+        op.ol[i][j] = Oc[j];
       }
     }
     const float* Gc = in.gam + 32 * w + 4 * lg;
@@ -610,18 +650,23 @@ struct ScanStep {
   }
 
   // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
-  // S = diag(Gam) S + Kg^T V.  Two workgroup barriers.
+  // S = diag(Gam) S + Kg^T V.  Two workgroup barriers.  ALL: every wave of the
+  // workgroup holds a dk slice (no idle waves), which keeps the step free of
+  // divergent branches so the compiler can count outstanding loads exactly.
+  template <bool ALL>
   static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[2], const Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
-                                              int jb, int start, int len) {
+                                              int jb) {
+    const int start = __builtin_amdgcn_readfirstlane(op.start);
+    const int len = __builtin_amdgcn_readfirstlane(op.len);
     f32x4* red_v = reinterpret_cast<f32x4*>(lds);                    // [KBD][TT][64]
     f32x4* red_o = reinterpret_cast<f32x4*>(lds + Gm::SCAN_RED);      // [KBD][TT][64]
     TIO* Vt = reinterpret_cast<TIO*>(lds + 2 * Gm::SCAN_RED);         // [16][VT_LD]
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
+    const bool active = ALL || w < KBD;
 
-    const bool active = w < KBD;  // waves past the dk slices only keep the barriers
     if (active) {
       const FragT sb = frag_from_d<TIO>(S[0], S[1]);
 #pragma unroll
@@ -631,10 +676,13 @@ struct ScanStep {
       }
     }
     __syncthreads();
+    // the chunk's rows of o as one raw buffer: rows >= len fall outside it
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
       const int t = w + KBD * i;
-      if (active && t < TT) {
+      if (active && (TT % KBD == 0 || t < TT)) {
         f32x4 vv, oo;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -650,8 +698,9 @@ struct ScanStep {
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * t + 4 * lg + j;
           Vt[l16 * VT_LD + r] = from_f32<TIO>(vv[j]);
-          if (r < len)
-            o[(int64_t)(start + r) * ostride + (int64_t)h * D + 16 * jb + l16] = from_f32<TIO>(oo[j]);
+          const int off =
+              r < len ? (r * (int)ostride + h * D + 16 * jb + l16) * (int)sizeof(TIO) : kBufferOff;
+          buffer_store(from_f32<TIO>(oo[j]), orsrc, off);
         }
       }
     }

@@ -90,6 +90,13 @@ __device__ __forceinline__ f32x8 load_frag8<float>(const float* p) {
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Store 8 consecutive elements (two 16-byte halves for fp32).
+__device__ __forceinline__ void store_frag8(bf16* p, bf16x8 f) { *reinterpret_cast<bf16x8*>(p) = f; }
+__device__ __forceinline__ void store_frag8(float* p, f32x8 f) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
 // Fragment in kperm order from a row: elements p[base + 4g + 0..3] and
 // p[base + 16 + 4g + 0..3] (base = 32 * slice); two 4-element loads.
 template <typename T>
@@ -121,5 +128,19 @@ __device__ __forceinline__ typename Frag<T>::type frag_from_d(f32x4 d0, f32x4 d1
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer stores: a lane whose byte offset is at or past the buffer's
+// num_records has its store dropped by the hardware, so a masked store needs
+// no branch.  kBufferOff is such an offset.
+constexpr int kBufferOff = (int)0x80000000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buffer_store(bf16 v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store(float v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+}
 
 }  // namespace kda

@@ -156,24 +156,38 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Two-pass plan, stage 1: chunk-local stage for every (chunk, head).
+// Two-pass plan, stage 1: chunk-local stage for every (chunk, head).  A
+// persistent grid (one workgroup per CU) walks the (chunk, head) items; the
+// next item's inputs are loaded while the current one computes.
 template <typename TIO, int D, int C>
-__global__ __launch_bounds__(256) void chunk_local_kernel(
+__global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     const float* __restrict__ g, const TIO* __restrict__ beta, int n_heads, float scale,
     const int* __restrict__ chunk_total, const ChunkEnt* __restrict__ tab,
     unsigned char* __restrict__ blocks) {
   using CL = ChunkLocal<TIO, D, C>;
-  const int ci = blockIdx.x;
-  const int h = blockIdx.y;
-  if (ci >= *chunk_total) return;
-  const ChunkEnt ent = tab[ci];
+  using Gm = Geo<TIO, D, C>;
   extern __shared__ __align__(16) unsigned char lds[];
-  typename CL::Inputs in;
-  CL::prefetch(in, q, k, v, g, beta, n_heads, h, ent.start, ent.len);
-  const ChunkOut<TIO> out =
-      chunk_out_at<TIO, D, C>(blocks + ((size_t)ci * n_heads + h) * Geo<TIO, D, C>::OUT_BYTES);
-  CL::run(lds, in, scale, out, q, k, g, n_heads, h);
+  const int n_items = *chunk_total * n_heads;
+  auto fetch = [&](typename CL::Inputs& in, int w) {
+    const ChunkEnt ent = tab[w / n_heads];
+    CL::prefetch(in, q, k, v, g, beta, n_heads, w % n_heads, ent.start, ent.len);
+  };
+  auto compute = [&](const typename CL::Inputs& in, int w) {
+    const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)w * Gm::OUT_BYTES);
+    CL::run(lds, in, scale, out, q, k, g, n_heads, w % n_heads);
+    __syncthreads();  // the next item overwrites the LDS
+  };
+  typename CL::Inputs cur, nxt;
+  int w = blockIdx.x;
+  if (w < n_items) fetch(cur, w);
+  while (w < n_items) {
+    const int w2 = w + gridDim.x;
+    if (w2 < n_items) fetch(nxt, w2);  // in flight during this item
+    compute(cur, w);
+    cur = nxt;
+    w = w2;
+  }
 }
 
 // Two-pass plan, stage 2: state scan with the output, one workgroup of D/32
@@ -215,14 +229,34 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   auto out_of = [&](int ci) {
     return chunk_out_at<TIO, D, C>(blocks + ((size_t)ci * n_heads + h) * Gm::OUT_BYTES);
   };
-  typename SS::Ops cur, nxt;
-  if (c_begin < c_end) SS::load(cur, out_of(c_begin), jb);
+  // Three chunks of operators in flight: each buffer keeps its role across the
+  // unrolled loop, so no load waits on a later one.
+  // Loads past the sequence's last chunk are clamped to it (read, then
+  // unused), so every path issues the same loads and the compiler's wait
+  // counts stay exact.
+  typename SS::Ops b0, b1, b2;
+  auto fetch = [&](typename SS::Ops& buf, int ci) {
+    ci = ci < c_end ? ci : c_end - 1;
+    SS::template load<true>(buf, out_of(ci), jb);
+    buf.start = tab[ci].start;
+    buf.len = tab[ci].len;
+  };
+  if (c_begin < c_end) {
+    fetch(b0, c_begin + 0);
+    fetch(b1, c_begin + 1);
+    fetch(b2, c_begin + 2);
+  }
   __syncthreads();
-  for (int ci = c_begin; ci < c_end; ++ci) {
-    if (ci + 1 < c_end) SS::load(nxt, out_of(ci + 1), jb);
-    const ChunkEnt ent = tab[ci];
-    SS::step(lds, S, cur, o, ostride, h, jb, ent.start, ent.len);
-    cur = nxt;
+  auto run_step = [&](typename SS::Ops& buf, int ci) {
+    SS::template step<true>(lds, S, buf, o, ostride, h, jb);
+    fetch(buf, ci + 3);
+  };
+  for (int ci = c_begin; ci < c_end; ci += 3) {
+    run_step(b0, ci);
+    if (ci + 1 >= c_end) break;
+    run_step(b1, ci + 1);
+    if (ci + 2 >= c_end) break;
+    run_step(b2, ci + 2);
   }
   if (ht) {
 #pragma unroll
@@ -292,7 +326,7 @@ __device__ __forceinline__ int spin_until_geq(const int* p, int target, int* sta
 }
 
 template <typename TIO, int D, int C>
-__global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
   using Gm = Geo<TIO, D, C>;
   using CL = ChunkLocal<TIO, D, C>;
   using SS = ScanStep<TIO, D, C>;
@@ -429,12 +463,13 @@ __global__ __launch_bounds__(256) void fused_kernel(FusedArgs a) {
     if (!s_ok) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     SS::clear_vt(lds);  // the chunk-local stage used this LDS
-    if (s0 == 0) SS::load(cur, slot_out(0), jb);
+    if (s0 == 0) SS::template load<false>(cur, slot_out(0), jb);
     __syncthreads();
     for (int s = s0; s < s1; ++s) {
-      if (s + 1 < sw) SS::load(nxt, slot_out(s + 1), jb);
-      const ChunkEnt ent = a.tab[cc.ci];
-      SS::step(lds, S, cur, o, ostride, cc.h, jb, ent.start, ent.len);
+      if (s + 1 < sw) SS::template load<false>(nxt, slot_out(s + 1), jb);
+      cur.start = a.tab[cc.ci].start;
+      cur.len = a.tab[cc.ci].len;
+      SS::template step<false>(lds, S, cur, o, ostride, cc.h, jb);
       cur = nxt;
       ++cc.ci;
       if (cc.ci >= cc.ce) {  // task finished
@@ -463,8 +498,8 @@ int fused_teams(int n_seqs, int n_heads) {
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)Gm::FUSED_LDS) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<TIO, D, C>, 256,
-                                                   Gm::FUSED_LDS) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<TIO, D, C>,
+                                                   kLocalThreads, Gm::FUSED_LDS) != hipSuccess)
     return 0;
   const int tasks = n_seqs * n_heads;
   int nteams = cus * per_cu / NB;
@@ -526,8 +561,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
       fa.ring = ws + L.off_ring;
       void* args[] = {&fa};
       err = hipLaunchCooperativeKernel((const void*)fused_kernel<TIO, D, C>,
-                                       dim3((unsigned)(nteams * (D / 16))), dim3(256), args,
-                                       (unsigned)Gm::FUSED_LDS, stream);
+                                       dim3((unsigned)(nteams * (D / 16))), dim3(kLocalThreads),
+                                       args, (unsigned)Gm::FUSED_LDS, stream);
       if (err != hipSuccess) return err;
       if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
       if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
@@ -538,8 +573,15 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
     err = hipFuncSetAttribute((const void*)chunk_local_kernel<TIO, D, C>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)Gm::LOCAL_LDS);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C>), dim3((unsigned)ntu, (unsigned)a.n_heads),
-                       dim3(256), Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
+    int dev = 0, cus = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
+        hipSuccess)
+      return err;
+    const int64_t items = ntu * a.n_heads;
+    const unsigned grid = (unsigned)(items < cus ? items : cus);
+    hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C>), dim3(grid), dim3(kLocalThreads),
+                       Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
                        (const TIO*)a.v, a.g, (const TIO*)a.beta, a.n_heads, a.scale,
                        chunk_off + a.n_seqs, tab, blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
