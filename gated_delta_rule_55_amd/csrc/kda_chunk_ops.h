@@ -150,14 +150,21 @@ struct ChunkLocal {
   static constexpr int GPR = D / 4;                 // float4 per row of g
   static constexpr int NG = (C * GPR + NT - 1) / NT;  // float4 per thread of g
 
-  // The chunk's inputs as this thread loads them (rows beyond L are zero).
+  // The chunk's inputs as this thread loads them.  Every load is issued
+  // unconditionally (rows at or past L re-read row L - 1; L >= 1) and the
+  // masking happens when the registers are staged, so the compiler can count
+  // the loads in flight and never has to wait for the whole prefetch early.
   struct Inputs {
     uint4 k[NV], q[NV], v[NV];
     f32x4 g[NG];
-    float beta;
+    TIO beta;
     int64_t tok0;
     int len;
   };
+
+  static __device__ __forceinline__ uint4 mask4(uint4 a, unsigned mk) {
+    return uint4{a.x & mk, a.y & mk, a.z & mk, a.w & mk};
+  }
 
   // Issue every global load of one (chunk, head); nothing waits on them here.
   static __device__ __forceinline__ void prefetch(Inputs& in, const TIO* __restrict__ q,
@@ -172,26 +179,22 @@ struct ChunkLocal {
     in.len = L;
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
-      const int x = tid + NT * m;
-      const int r = x / VPR, cv = x % VPR;
-      in.k[m] = in.q[m] = in.v[m] = uint4{0, 0, 0, 0};
-      if (x < C * VPR && r < L) {
-        const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
-        in.k[m] = reinterpret_cast<const uint4*>(k + off)[cv];
-        in.q[m] = reinterpret_cast<const uint4*>(q + off)[cv];
-        in.v[m] = reinterpret_cast<const uint4*>(v + off)[cv];
-      }
+      const int x0 = tid + NT * m;
+      const int x = x0 < C * VPR ? x0 : C * VPR - 1;
+      const int r = min(x / VPR, L - 1), cv = x % VPR;
+      const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
+      in.k[m] = reinterpret_cast<const uint4*>(k + off)[cv];
+      in.q[m] = reinterpret_cast<const uint4*>(q + off)[cv];
+      in.v[m] = reinterpret_cast<const uint4*>(v + off)[cv];
     }
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
-      const int x = tid + NT * m;
-      const int r = x / GPR, cv = x % GPR;
-      in.g[m] = zero4();
-      if (x < C * GPR && r < L)
-        in.g[m] = reinterpret_cast<const f32x4*>(g + (tok0 + r) * rs + (int64_t)h * D)[cv];
+      const int x0 = tid + NT * m;
+      const int x = x0 < C * GPR ? x0 : C * GPR - 1;
+      const int r = min(x / GPR, L - 1), cv = x % GPR;
+      in.g[m] = reinterpret_cast<const f32x4*>(g + (tok0 + r) * rs + (int64_t)h * D)[cv];
     }
-    in.beta = 0.f;
-    if (tid < C && tid < L) in.beta = to_f32(beta[(tok0 + tid) * n_heads + h]);
+    in.beta = beta[(tok0 + min(tid, L - 1)) * n_heads + h];
   }
 
   // Entry-by-entry Gram tile from the inputs in global memory, for a diagonal
@@ -282,14 +285,17 @@ struct ChunkLocal {
     constexpr int NGRP = (C / 8) * D / NT > 0 ? (C / 8) * D / NT : 1;
 
     // ---- phase 0: stage k, q, v, g (base 2) and beta; clear padding --------
+    // rows at or past the chunk's length are staged as zeros (bit masks, so
+    // the registers are never selected by address)
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int x = tid + NT * m;
       if (x < C * VPR) {
         const int r = x / VPR, cv = x % VPR;
-        reinterpret_cast<uint4*>(Lk + r * KS_LD)[cv] = in.k[m];
-        reinterpret_cast<uint4*>(Lq + r * KS_LD)[cv] = in.q[m];
-        reinterpret_cast<uint4*>(Vs + r * KS_LD)[cv] = in.v[m];
+        const unsigned mk = r < in.len ? ~0u : 0u;
+        reinterpret_cast<uint4*>(Lk + r * KS_LD)[cv] = mask4(in.k[m], mk);
+        reinterpret_cast<uint4*>(Lq + r * KS_LD)[cv] = mask4(in.q[m], mk);
+        reinterpret_cast<uint4*>(Vs + r * KS_LD)[cv] = mask4(in.v[m], mk);
       }
     }
 #pragma unroll
@@ -297,10 +303,14 @@ struct ChunkLocal {
       const int x = tid + NT * m;
       if (x < C * GPR) {
         const int r = x / GPR, cv = x % GPR;
-        *reinterpret_cast<f32x4*>(Gs + r * GS_LD + 4 * cv) = in.g[m] * kLog2e;
+        const bool live = r < in.len;
+        f32x4 gv = in.g[m] * kLog2e;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv[e] = live ? gv[e] : 0.f;
+        *reinterpret_cast<f32x4*>(Gs + r * GS_LD + 4 * cv) = gv;
       }
     }
-    if (tid < C) s_beta[tid] = in.beta;
+    if (tid < C) s_beta[tid] = tid < in.len ? to_f32(in.beta) : 0.f;
     if (tid == 0) *s_flag = 0;
     {
       constexpr int NZ = C * TK_LD * (int)sizeof(TIO) / 16;  // uint4 per array

@@ -183,7 +183,9 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
   if (w < n_items) fetch(cur, w);
   while (w < n_items) {
     const int w2 = w + gridDim.x;
-    if (w2 < n_items) fetch(nxt, w2);  // in flight during this item
+    // in flight during this item (past the end: the last item again, unused),
+    // issued unconditionally so the compiler's load counts stay exact
+    fetch(nxt, w2 < n_items ? w2 : n_items - 1);
     compute(cur, w);
     cur = nxt;
     w = w2;
