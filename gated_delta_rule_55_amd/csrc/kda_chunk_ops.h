@@ -107,7 +107,9 @@ struct Geo {
   // Scan-step LDS (aliases the chunk-local region; the two never overlap).
   static constexpr int VT_LD = KCP + TP;
   static constexpr size_t SCAN_RED = (size_t)KBD * TT * 64 * 16;  // one of v / o partials
-  static constexpr size_t SCAN_LDS = 2 * SCAN_RED + (size_t)16 * VT_LD * sizeof(TIO);
+  static constexpr int OS_LD = 16 + TP;  // o staging rows: 16 value columns + pad
+  static constexpr size_t OFF_OS = align_up(2 * SCAN_RED + (size_t)16 * VT_LD * sizeof(TIO), 16);
+  static constexpr size_t SCAN_LDS = OFF_OS + (size_t)C * OS_LD * sizeof(TIO);
   static constexpr size_t FUSED_LDS = cmaxz(LOCAL_LDS, SCAN_LDS);
 
   static constexpr bool FITS = FUSED_LDS <= 160 * 1024;
@@ -625,23 +627,26 @@ struct ScanStep {
     int start, len;  // the chunk's token range (set by the caller)
   };
 
-  // ALL: every wave of the workgroup holds a dk slice.
+  // Loads of one chunk's operators, in three groups that a step consumes in
+  // turn (W and Q', then U and Ol, then Kg and Gam), so a step can refill each
+  // group as soon as it is done with it.  ALL: every wave of the workgroup
+  // holds a dk slice (else waves past the slices load nothing).
   template <bool ALL>
-  static __device__ __forceinline__ void load(Ops& op, const ChunkOut<TIO>& in, int jb) {
+  static __device__ __forceinline__ void load_wq(Ops& op, const ChunkOut<TIO>& in) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int lg = lane >> 4;
-    if (!ALL && w >= KBD) return;  // waves past the dk slices hold no state
+    if (!ALL && w >= KBD) return;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       op.w[t] = load_frag8<TIO>(in.w + ((size_t)(t * KBD + w) * 64 + lane) * 8);
       op.q[t] = load_frag8<TIO>(in.q + ((size_t)(t * KBD + w) * 64 + lane) * 8);
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int kc = 0; kc < KBC; ++kc)
-        op.k[m][kc] = load_frag8<TIO>(in.k + ((size_t)((2 * w + m) * KBC + kc) * 64 + lane) * 8);
+  }
+  template <bool ALL>
+  static __device__ __forceinline__ void load_uo(Ops& op, const ChunkOut<TIO>& in, int jb) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    if (!ALL && w >= KBD) return;
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
       const int t0 = w + KBD * i;
@@ -654,24 +659,51 @@ struct ScanStep {
         op.ol[i][j] = Oc[j];
       }
     }
+  }
+  template <bool ALL>
+  static __device__ __forceinline__ void load_kg(Ops& op, const ChunkOut<TIO>& in) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int lg = lane >> 4;
+    if (!ALL && w >= KBD) return;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int kc = 0; kc < KBC; ++kc)
+        op.k[m][kc] = load_frag8<TIO>(in.k + ((size_t)((2 * w + m) * KBC + kc) * 64 + lane) * 8);
     const float* Gc = in.gam + 32 * w + 4 * lg;
     op.gam[0] = *reinterpret_cast<const f32x4*>(Gc);
     op.gam[1] = *reinterpret_cast<const f32x4*>(Gc + 16);
+  }
+  template <bool ALL>
+  static __device__ __forceinline__ void load(Ops& op, const ChunkOut<TIO>& in, int jb) {
+    load_wq<ALL>(op, in);
+    load_uo<ALL>(op, in, jb);
+    load_kg<ALL>(op, in);
   }
 
   // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
   // S = diag(Gam) S + Kg^T V.  Two workgroup barriers.  ALL: every wave of the
   // workgroup holds a dk slice (no idle waves), which keeps the step free of
   // divergent branches so the compiler can count outstanding loads exactly.
-  template <bool ALL>
-  static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[2], const Ops& op,
+  // NTH: threads of the workgroup.  With `nxt` set, each group of `op` is
+  // reloaded from *nxt as soon as the step has consumed it (the loads then
+  // overlap the rest of the step); nxt_ent supplies the new token range.
+  // live = false (uniform) runs the step without effect: no o rows are
+  // written and S keeps its value; the refills still happen.
+  template <bool ALL, int NTH>
+  static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
-                                              int jb) {
+                                              int jb, const ChunkOut<TIO>* nxt = nullptr,
+                                              const ChunkEnt* nxt_ent = nullptr,
+                                              bool live = true) {
     const int start = __builtin_amdgcn_readfirstlane(op.start);
-    const int len = __builtin_amdgcn_readfirstlane(op.len);
+    const int len = live ? __builtin_amdgcn_readfirstlane(op.len) : 0;
+    const f32x4 s_keep[2] = {S[0], S[1]};
     f32x4* red_v = reinterpret_cast<f32x4*>(lds);                    // [KBD][TT][64]
     f32x4* red_o = reinterpret_cast<f32x4*>(lds + Gm::SCAN_RED);      // [KBD][TT][64]
     TIO* Vt = reinterpret_cast<TIO*>(lds + 2 * Gm::SCAN_RED);         // [16][VT_LD]
+    TIO* Os = reinterpret_cast<TIO*>(lds + Gm::OFF_OS);               // [C][OS_LD]
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -685,10 +717,8 @@ struct ScanStep {
         red_o[(w * TT + t) * 64 + lane] = mma32(op.q[t], sb, zero4());
       }
     }
+    if (nxt) load_wq<ALL>(op, *nxt);
     __syncthreads();
-    // the chunk's rows of o as one raw buffer: rows >= len fall outside it
-    const __amdgpu_buffer_rsrc_t orsrc =
-        make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
 #pragma unroll
     for (int i = 0; i < NOWN; ++i) {
       const int t = w + KBD * i;
@@ -708,23 +738,50 @@ struct ScanStep {
         for (int j = 0; j < 4; ++j) {
           const int r = 16 * t + 4 * lg + j;
           Vt[l16 * VT_LD + r] = from_f32<TIO>(vv[j]);
-          const int off =
-              r < len ? (r * (int)ostride + h * D + 16 * jb + l16) * (int)sizeof(TIO) : kBufferOff;
-          buffer_store(from_f32<TIO>(oo[j]), orsrc, off);
+          Os[r * Gm::OS_LD + l16] = from_f32<TIO>(oo[j]);
         }
       }
     }
+    if (nxt) load_uo<ALL>(op, *nxt, jb);
     __syncthreads();
-    if (!active) return;
+    {
+      // the chunk's rows of o as one raw buffer: rows >= len fall outside it;
+      // 16-byte pieces, EPV values of one row each
+      constexpr int EPV = 16 / (int)sizeof(TIO), VPRO = 16 / EPV, NVEC = C * VPRO;
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      S[m] *= op.gam[m];
-#pragma unroll
-      for (int kc = 0; kc < KBC; ++kc) {
-        // Kg fragments are in kperm token order; read V the same way
-        const FragT fv = load_frag_perm<TIO>(Vt + l16 * VT_LD + 32 * kc, lg);
-        S[m] = mma32(op.k[m][kc], fv, S[m]);
+      for (int p = 0; p < (NVEC + NTH - 1) / NTH; ++p) {
+        const int x0 = (int)threadIdx.x + NTH * p;
+        const int x = x0 < NVEC ? x0 : NVEC - 1;
+        const int r = x / VPRO, cv = x % VPRO;
+        const uint4 val = *reinterpret_cast<const uint4*>(Os + r * Gm::OS_LD + cv * EPV);
+        const int off = (x0 < NVEC && r < len)
+                            ? (r * (int)ostride + h * D + 16 * jb + cv * EPV) * (int)sizeof(TIO)
+                            : kBufferOff;
+        buffer_store16(val, orsrc, off);
       }
+    }
+    if (active) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        S[m] *= op.gam[m];
+#pragma unroll
+        for (int kc = 0; kc < KBC; ++kc) {
+          // Kg fragments are in kperm token order; read V the same way
+          const FragT fv = load_frag_perm<TIO>(Vt + l16 * VT_LD + 32 * kc, lg);
+          S[m] = mma32(op.k[m][kc], fv, S[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[m][j] = live ? S[m][j] : s_keep[m][j];
+    }
+    if (nxt) {
+      load_kg<ALL>(op, *nxt);
+      op.start = nxt_ent->start;
+      op.len = nxt_ent->len;
     }
   }
 

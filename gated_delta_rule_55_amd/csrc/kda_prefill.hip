@@ -223,8 +223,20 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      S[m][j] = h0 ? h0[sbase + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      // no h0: an empty buffer, whose loads read 0 (branch-free, so the
+      // compiler keeps exact counts of the loads in flight)
+      const __amdgpu_buffer_rsrc_t hr =
+          make_rsrc(const_cast<float*>(h0 ? h0 + sbase : h0), h0 ? D * D * 4 : 0);
+      S[m][j] = buffer_load_f32(hr, ((32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16) * 4);
+    }
+  // Take delivery of h0 here, before the operator loads are issued: S then
+  // enters the loop with nothing in flight, and the loop's own waits are
+  // counted exactly (an empty asm that reads and writes S; emits nothing).
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(S[m][j]));
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const int64_t ostride = (int64_t)n_heads * D;
@@ -235,10 +247,14 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   // unrolled loop, so no load waits on a later one.
   // Loads past the sequence's last chunk are clamped to it (read, then
   // unused), so every path issues the same loads and the compiler's wait
-  // counts stay exact.
+  // counts stay exact.  Three chunks of operators are in flight: each buffer
+  // keeps its role across the unrolled loop, and a step refills its buffer
+  // with the chunk three ahead piece by piece as it consumes it.
+  constexpr int NTH = 64 * (D / 32);
   typename SS::Ops b0, b1, b2;
+  auto clamp = [&](int ci) { return ci < c_end ? ci : c_end - 1; };
   auto fetch = [&](typename SS::Ops& buf, int ci) {
-    ci = ci < c_end ? ci : c_end - 1;
+    ci = clamp(ci);
     SS::template load<true>(buf, out_of(ci), jb);
     buf.start = tab[ci].start;
     buf.len = tab[ci].len;
@@ -249,15 +265,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     fetch(b2, c_begin + 2);
   }
   __syncthreads();
+  // The loop body runs its three steps unconditionally (a step past the last
+  // chunk has no effect), so the body is one basic block and the compiler
+  // cannot sink a refill toward the next iteration.
   auto run_step = [&](typename SS::Ops& buf, int ci) {
-    SS::template step<true>(lds, S, buf, o, ostride, h, jb);
-    fetch(buf, ci + 3);
+    const int cn = clamp(ci + 3);
+    const ChunkOut<TIO> nx = out_of(cn);
+    SS::template step<true, NTH>(lds, S, buf, o, ostride, h, jb, &nx, tab + cn, ci < c_end);
   };
   for (int ci = c_begin; ci < c_end; ci += 3) {
     run_step(b0, ci);
-    if (ci + 1 >= c_end) break;
     run_step(b1, ci + 1);
-    if (ci + 2 >= c_end) break;
     run_step(b2, ci + 2);
   }
   if (ht) {
@@ -471,7 +489,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
       if (s + 1 < sw) SS::template load<false>(nxt, slot_out(s + 1), jb);
       cur.start = a.tab[cc.ci].start;
       cur.len = a.tab[cc.ci].len;
-      SS::template step<false>(lds, S, cur, o, ostride, cc.h, jb);
+      SS::template step<false, kLocalThreads>(lds, S, cur, o, ostride, cc.h, jb);
       cur = nxt;
       ++cc.ci;
       if (cc.ci >= cc.ce) {  // task finished
