@@ -53,6 +53,10 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
   if (d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
     return KDA_ERR_UNSUPPORTED;
+  // The fused plan is switched off: its workgroups wait on each other, and a
+  // run of it left a GPU unusable without an explained cause.  It stays
+  // rejected here, before anything is launched, until that is understood.
+  if (d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
   a->plan = d->plan;
   a->n_seqs = d->n_seqs;

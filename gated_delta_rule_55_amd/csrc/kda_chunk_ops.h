@@ -135,6 +135,35 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Lane moves within a row of 16 lanes (DPP).  Lanes without a source read 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// Value of lane i of this lane's 16-lane row (row_newbcast:i); i a constant
+// after unrolling.
+__device__ __forceinline__ float row_bcast(float x, int i) {
+  switch (i) {
+    case 0: return dpp<0x150>(x);
+    case 1: return dpp<0x151>(x);
+    case 2: return dpp<0x152>(x);
+    case 3: return dpp<0x153>(x);
+    case 4: return dpp<0x154>(x);
+    case 5: return dpp<0x155>(x);
+    case 6: return dpp<0x156>(x);
+    case 7: return dpp<0x157>(x);
+    case 8: return dpp<0x158>(x);
+    case 9: return dpp<0x159>(x);
+    case 10: return dpp<0x15A>(x);
+    case 11: return dpp<0x15B>(x);
+    case 12: return dpp<0x15C>(x);
+    case 13: return dpp<0x15D>(x);
+    case 14: return dpp<0x15E>(x);
+    default: return dpp<0x15F>(x);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Chunk-local stage.
 template <typename TIO, int D, int C>
@@ -485,24 +514,40 @@ struct ChunkLocal {
     __syncthreads();
 
     // ---- phase 4: T = (I + A)^-1 ------------------------------------------
-    // Diagonal 16x16 blocks by forward substitution in wave 0 (lane = block
-    // lg, column l16); then the off-diagonal blocks one band at a time, one
-    // wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb  (fp32 MFMA).
-    if (wave == 0 && lg < TT) {
-      const int a = lg, j = l16;
-      float x[16];
+    // Diagonal 16x16 blocks in wave 0, lane 16a + r holding row r of block a:
+    // column-oriented substitution, row i of the inverse reaching the rows
+    // below it by a row broadcast; then the off-diagonal blocks one band at
+    // a time, one wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
+    // (fp32 MFMA).
+    if (wave == 0) {
+      const int a = lg < TT ? lg : TT - 1;  // rows past the blocks: a copy, unused
+      const int r = l16;
+      float Ar[16], X[16];
+      const float* arow = As + (16 * a + r) * AF_LD + 16 * a;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* Ar = As + (16 * a + r) * AF_LD + 16 * a;
-        float acc = (r == j) ? 1.f : 0.f;
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(arow + 4 * j4);
 #pragma unroll
-        for (int i = 0; i < r; ++i) acc -= Ar[i] * x[i];
-        x[r] = acc;
+        for (int e = 0; e < 4; ++e) Ar[4 * j4 + e] = x4[e];
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        Ts[(16 * a + r) * AF_LD + 16 * a + j] = x[r];
-        Tb[(16 * a + r) * TK_LD + 16 * a + j] = from_f32<TIO>(x[r]);
+      for (int j = 0; j < 16; ++j) X[j] = (j == r) ? 1.f : 0.f;
+      // A is strictly lower triangular: rows r <= i see a zero multiplier
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        const float m = -Ar[i];
+#pragma unroll
+        for (int j = 0; j <= i; ++j) X[j] = fmaf(m, row_bcast(X[j], i), X[j]);
+      }
+      if (lg < TT) {
+        float* trow = Ts + (16 * a + r) * AF_LD + 16 * a;
+        TIO* brow = Tb + (16 * a + r) * TK_LD + 16 * a;
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4)
+          *reinterpret_cast<f32x4*>(trow + 4 * j4) =
+              f32x4{X[4 * j4], X[4 * j4 + 1], X[4 * j4 + 2], X[4 * j4 + 3]};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) brow[j] = from_f32<TIO>(X[j]);
       }
     }
     __syncthreads();

@@ -58,7 +58,7 @@ typedef enum {
   KDA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be,
                                or too large                                    */
   KDA_ERR_DTYPE = -3,       /* dtype is not one of kda_dtype                   */
-  KDA_ERR_UNSUPPORTED = -4, /* head dim or chunk size not supported           */
+  KDA_ERR_UNSUPPORTED = -4, /* head dim, chunk size or plan not supported     */
   KDA_ERR_ALIGN = -5,       /* a pointer breaks its alignment rule (below)     */
   KDA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
   KDA_ERR_HIP = -7,         /* a HIP launch failed; see kda_last_hip_error()   */
@@ -73,13 +73,11 @@ typedef enum {
 
 typedef enum { KDA_DTYPE_F32 = 1, KDA_DTYPE_BF16 = 2 } kda_dtype;
 
-/* Launch plan of the chunked prefill.  FUSED runs the whole pass as one
- * cooperative kernel whose chunk-local results stay on chip; TWO_PASS writes
- * them to the workspace and reads them back (same results up to rounding
- * order within a chunk step: both use the same arithmetic).  AUTO currently
- * selects TWO_PASS, the faster of the two on MI355X as measured.  An explicit
- * FUSED that cannot be honoured (the grid does not fit on the device at once)
- * returns KDA_ERR_HIP. */
+/* Launch plan of the chunked prefill.  TWO_PASS writes the chunk-local
+ * results to the workspace and reads them back in the state scan; AUTO
+ * selects it.  FUSED (one cooperative kernel whose chunk-local results stay
+ * in a cache-resident ring) is currently switched off: a request for it
+ * returns KDA_ERR_UNSUPPORTED before anything is launched. */
 typedef enum { KDA_PLAN_AUTO = 0, KDA_PLAN_FUSED = 1, KDA_PLAN_TWO_PASS = 2 } kda_plan;
 
 /* Chunked prefill over a packed batch of N sequences (T_total tokens).

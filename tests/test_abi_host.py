@@ -115,6 +115,16 @@ def test_prefill_rejects_bad_pointers(abi, over, status):
 
 
 @no_gpu_only
+def test_fused_plan_is_switched_off(abi):
+    """A fused-plan request is refused on the host, before any launch."""
+    d = _valid_prefill(abi, plan=abi.KDA_PLAN_FUSED)
+    st = ctypes.c_int(0)
+    abi.lib().kda_chunk_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(st))
+    assert st.value == abi.KDA_ERR_UNSUPPORTED
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == abi.KDA_ERR_UNSUPPORTED
+
+
+@no_gpu_only
 def test_prefill_rejects_small_or_missing_workspace(abi):
     d = _valid_prefill(abi)
     need = abi.workspace_bytes(d)

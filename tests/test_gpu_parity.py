@@ -32,6 +32,12 @@ def run_prefill(kda, inp, chunk=None, ht_inplace=False, plan="auto"):
     return to_host64(o), to_host64(hT)
 
 
+# The fused plan is switched off in the library (a request for it returns
+# KDA_ERR_UNSUPPORTED): a run of it left a GPU unusable without an explained
+# cause, so its cases stay skipped until that is understood.
+FUSED_OFF = "fused plan switched off pending review of its inter-workgroup waits"
+
+
 @pytest.mark.parametrize("dtype,d,chunk,lengths,h0", [
     ("f32", 32, 16, [128], False),        # the tiny fp32 workload
     ("f32", 64, 32, [77, 0, 130], True),
@@ -43,7 +49,8 @@ def run_prefill(kda, inp, chunk=None, ht_inplace=False, plan="auto"):
     ("bf16", 128, 16, [90, 17], True),
     ("bf16", 128, 32, [150], False),
 ])
-@pytest.mark.parametrize("plan", ["fused", "two_pass"])
+@pytest.mark.parametrize("plan", [pytest.param("fused", marks=pytest.mark.skip(reason=FUSED_OFF)),
+                                  "two_pass"])
 def test_prefill_small(kda, dtype, d, chunk, lengths, h0, plan):
     say(f"prefill plan={plan} dtype={dtype} d={d} C={chunk} lengths={lengths} h0={h0}")
     inp = synth.make_inputs(11, lengths, 3, d, dtype=dtype,
@@ -56,6 +63,7 @@ def test_prefill_small(kda, dtype, d, chunk, lengths, h0, plan):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.skip(reason=FUSED_OFF)
 @pytest.mark.parametrize("lengths", [[300], [64, 1, 129, 0, 200, 640], [0, 0]])
 def test_plans_agree_bitwise(kda, lengths):
     """The fused and two-pass plans run the same arithmetic in the same order,
