@@ -36,6 +36,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # Algorithmic traffic per token, bf16 inputs, H = 32, d = 128: q, k, v (bf16),
 # g (fp32), beta (bf16) read once, o (bf16) written once.
 BYTES_PER_TOKEN = 3 * 8192 + 16384 + 64 + 8192  # 49,216
+# With the gate fused: g (fp32, 16,384 B/token) is replaced by the raw gate x (bf16).
+BYTES_PER_TOKEN_GATED = 3 * 8192 + 8192 + 64 + 8192  # 41,024
 STATE_BYTES = 32 * 128 * 128 * 4  # one sequence's h0 or hT
 # Algorithmic flops per (64-token chunk, head) of the chunked form.
 FLOPS_PER_CHUNK_HEAD = 9_041_236
@@ -85,12 +87,21 @@ def to_dev(arr, torch):
     return torch.from_numpy(arr).cuda()
 
 
-def bench_prefill(args, torch, kda, synth):
-    log("generating the prefill-32k inputs (seeded numpy)")
-    inp = synth.make_config(2)
+def bench_prefill(args, torch, kda, synth, inp=None, fused_gate=False):
+    """Time the prefill-32k pass.  fused_gate: pass the raw gate (x bf16,
+    a_log, dt_bias) instead of g, so the kernels compute the gate activation."""
+    if inp is None:
+        log("generating the prefill-32k inputs (seeded numpy)")
+        inp = synth.make_config(2)
     T, H, D = inp.T, inp.H, inp.dk
     q, k, v = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v))
-    g, beta = to_dev(inp.g, torch), to_dev(inp.beta, torch)
+    beta = to_dev(inp.beta, torch)
+    if fused_gate:
+        g = None
+        gate = (to_dev(inp.gate_x, torch), to_dev(inp.gate_a_log, torch),
+                to_dev(inp.gate_dt_bias, torch))
+    else:
+        g, gate = to_dev(inp.g, torch), None
     h0 = to_dev(inp.h0, torch)
     o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
     ht = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
@@ -104,7 +115,7 @@ def bench_prefill(args, torch, kda, synth):
 
     def run(events=None):
         kda.chunk_prefill(q, k, v, g, beta, h0, None, scale=inp.scale, chunk=64, out=o, ht=ht,
-                          workspace=ws, events=events, plan=args.plan)
+                          workspace=ws, events=events, plan=args.plan, gate=gate)
 
     for _ in range(args.warmup):
         run()
@@ -214,6 +225,7 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-gate", action="store_true", help="skip the fused-gate prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--plan", choices=["auto", "fused", "two_pass"], default="auto",
                     help="prefill launch plan")
@@ -265,6 +277,21 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    if not args.no_gate:
+        # the same workload with the gate activation fused into the kernels:
+        # the pass reads the raw gate x (bf16) instead of g (fp32)
+        _, gms_step, gstage = bench_prefill(args, torch, kda, synth, inp=inp, fused_gate=True)
+        gbytes = T * BYTES_PER_TOKEN_GATED + 2 * STATE_BYTES + H * 4 + H * D * 4
+        gach = gbytes / (gstage["prefill_call"] / 1e3) / 1e9
+        line["fused_gate"] = {
+            "workload": "prefill-32k with the gate activation fused: raw gate x bf16 "
+                        "[T, H, dk], a_log fp32 [H], dt_bias fp32 [H, dk] instead of g fp32",
+            "tokens_per_s": round(T / (gms_step / 1e3), 1), "ms_per_step": round(gms_step, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "scope": f"whole prefill pass, {gbytes} algorithmic bytes per pass"},
+            "kernels_ms": {kname: round(v, 4) for kname, v in gstage.items()},
+        }
     if not args.no_decode:
         dinp, S, dms, dec = bench_decode(args, torch, kda, synth)
         step_ms = dms / S

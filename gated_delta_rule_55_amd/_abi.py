@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
-KDA_ABI_VERSION = 1
+KDA_ABI_VERSION = 2
 KDA_OK = 0
 KDA_ERR_NULL = -1
 KDA_ERR_SHAPE = -2
@@ -28,6 +28,18 @@ KDA_PLAN_TWO_PASS = 2
 
 KDA_DTYPE_F32 = 1
 KDA_DTYPE_BF16 = 2
+
+KDA_GATE_GIVEN = 0
+KDA_GATE_KIMI = 1
+
+
+class GateDesc(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("x", ctypes.c_void_p),
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+    ]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -51,6 +63,7 @@ class PrefillDesc(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p),
         ("o", ctypes.c_void_p),
         ("ht", ctypes.c_void_p),
+        ("gate", GateDesc),
     ]
 
 
@@ -70,6 +83,7 @@ class DecodeDesc(ctypes.Structure):
         ("g", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("o", ctypes.c_void_p),
+        ("gate", GateDesc),
     ]
 
 
@@ -122,20 +136,26 @@ def status_string(status: int) -> str:
     return lib().kda_status_string(int(status)).decode()
 
 
+def _fill(d, kw):
+    for key, val in kw.items():
+        if key == "gate":  # (mode, x, a_log, dt_bias)
+            mode, x, a_log, dt_bias = val
+            d.gate = GateDesc(mode, x, a_log, dt_bias)
+        else:
+            setattr(d, key, val)
+    return d
+
+
 def prefill_desc(**kw) -> PrefillDesc:
     d = PrefillDesc()
     d.struct_size = ctypes.sizeof(PrefillDesc)
-    for key, val in kw.items():
-        setattr(d, key, val)
-    return d
+    return _fill(d, kw)
 
 
 def decode_desc(**kw) -> DecodeDesc:
     d = DecodeDesc()
     d.struct_size = ctypes.sizeof(DecodeDesc)
-    for key, val in kw.items():
-        setattr(d, key, val)
-    return d
+    return _fill(d, kw)
 
 
 def workspace_bytes(desc: PrefillDesc) -> int:

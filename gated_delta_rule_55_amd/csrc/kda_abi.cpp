@@ -38,6 +38,34 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.l
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 
+// The decay input of a descriptor: g (fp32), or the raw gate x (element size
+// es) with a_log [H] and dt_bias [H, D].  `rows` = tokens (prefill) or
+// sequences (decode).  Fills the ranges the call reads.
+int check_gate(const kda_gate_desc& gt, const float* g, bool work, int64_t rows, int64_t H,
+               int64_t D, int64_t es, kda::GateArgs* out, Range (&r)[3]) {
+  r[0] = r[1] = r[2] = Range{0, 0};
+  if (gt.mode == KDA_GATE_GIVEN) {
+    if (work && !g) return KDA_ERR_NULL;
+    if (g && !aligned(g, 4)) return KDA_ERR_ALIGN;
+    r[0] = range_of(g, rows * H * D * 4);
+    *out = kda::GateArgs{};
+    return KDA_OK;
+  }
+  if (gt.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
+  if (work && (!gt.x || !gt.a_log || !gt.dt_bias)) return KDA_ERR_NULL;
+  if ((gt.x && !aligned(gt.x, (uintptr_t)es)) || (gt.a_log && !aligned(gt.a_log, 4)) ||
+      (gt.dt_bias && !aligned(gt.dt_bias, 4)))
+    return KDA_ERR_ALIGN;
+  r[0] = range_of(gt.x, rows * H * D * es);
+  r[1] = range_of(gt.a_log, H * 4);
+  r[2] = range_of(gt.dt_bias, H * D * 4);
+  out->mode = kda::GATE_KIMI_;
+  out->x = gt.x;
+  out->a_log = gt.a_log;
+  out->dt_bias = gt.dt_bias;
+  return KDA_OK;
+}
+
 // Shared checks of the prefill descriptor; fills `a` on success.
 int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   if (!d) return KDA_ERR_NULL;
@@ -53,6 +81,7 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
   if (d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
     return KDA_ERR_UNSUPPORTED;
+  if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
   // The fused plan is switched off: its workgroups wait on each other, and a
   // run of it left a GPU unusable without an explained cause.  It stays
   // rejected here, before anything is launched, until that is understood.
@@ -77,38 +106,42 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   return KDA_OK;
 }
 
-int check_prefill_pointers(const kda_prefill_desc* d, const kda::PrefillArgs& a) {
+// Checks the pointers; on success `rin` holds every input range the call
+// reads (q, k, v, the decay input (3), beta, h0, cu_seqlens).
+int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range (&rin)[9]) {
   if (!d->cu_seqlens && d->n_seqs != 1) return KDA_ERR_NULL;
-  if (d->t_total > 0 && (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->o))
-    return KDA_ERR_NULL;
+  if (d->t_total > 0 && (!d->q || !d->k || !d->v || !d->beta || !d->o)) return KDA_ERR_NULL;
   // q and k rows are read as 16-byte vectors; everything else element-wise.
   const uintptr_t es_al = d->dtype == KDA_DTYPE_BF16 ? 2 : 4;
   if ((d->q && !aligned(d->q, 16)) || (d->k && !aligned(d->k, 16))) return KDA_ERR_ALIGN;
   const void* pe[] = {d->v, d->beta, d->o};
   for (const void* p : pe)
     if (p && !aligned(p, es_al)) return KDA_ERR_ALIGN;
-  const void* p4[] = {d->g, d->h0, d->ht, d->cu_seqlens};
+  const void* p4[] = {d->h0, d->ht, d->cu_seqlens};
   for (const void* p : p4)
     if (p && !aligned(p, 4)) return KDA_ERR_ALIGN;
 
-  const int64_t es = a.bf16 ? 2 : 4;
+  const int64_t es = a->bf16 ? 2 : 4;
   const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
+  Range rgate[3];
+  const int st = check_gate(d->gate, d->g, T > 0, T, H, D, es, &a->gate, rgate);
+  if (st != KDA_OK) return st;
   const Range rq = range_of(d->q, T * H * D * es), rk = range_of(d->k, T * H * D * es),
-              rv = range_of(d->v, T * H * D * es), rg = range_of(d->g, T * H * D * 4),
-              rb = range_of(d->beta, T * H * es), ro = range_of(d->o, T * H * D * es),
+              rv = range_of(d->v, T * H * D * es), rb = range_of(d->beta, T * H * es),
+              ro = range_of(d->o, T * H * D * es),
               rh0 = range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
               rht = range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
               rcu = range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0);
-  const Range inputs[] = {rq, rk, rv, rg, rb, rh0, rcu};
+  const Range inputs[9] = {rq, rk, rv, rgate[0], rgate[1], rgate[2], rb, rh0, rcu};
+  for (int i = 0; i < 9; ++i) rin[i] = inputs[i];
   for (const Range& r : inputs)
     if (overlap(ro, r)) return KDA_ERR_ALIAS;
   if (overlap(ro, rht)) return KDA_ERR_ALIAS;
   // ht may be exactly h0 (in-place carry) but may not partly overlap it, nor
   // overlap any other input.
   if (d->ht && d->h0 && d->ht != d->h0 && overlap(rht, rh0)) return KDA_ERR_ALIAS;
-  const Range others[] = {rq, rk, rv, rg, rb, rcu};
-  for (const Range& r : others)
-    if (overlap(rht, r)) return KDA_ERR_ALIAS;
+  for (const Range& r : inputs)
+    if (&r != &inputs[7] && overlap(rht, r)) return KDA_ERR_ALIAS;
   return KDA_OK;
 }
 
@@ -151,7 +184,8 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
   kda::PrefillArgs a;
   int st = check_prefill(d, &a);
   if (st != KDA_OK) return st;
-  st = check_prefill_pointers(d, a);
+  Range rin[9];
+  st = check_prefill_pointers(d, &a, rin);
   if (st != KDA_OK) return st;
   const size_t need = kda::prefill_workspace_bytes(a);
   if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
@@ -159,14 +193,11 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
   const Range rw = range_of(workspace, (int64_t)need);
   const int64_t es = a.bf16 ? 2 : 4;
   const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
-  const Range touched[] = {range_of(d->q, T * H * D * es), range_of(d->k, T * H * D * es),
-                           range_of(d->v, T * H * D * es), range_of(d->g, T * H * D * 4),
-                           range_of(d->beta, T * H * es), range_of(d->o, T * H * D * es),
-                           range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
-                           range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
-                           range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0)};
-  for (const Range& r : touched)
+  for (const Range& r : rin)
     if (overlap(rw, r)) return KDA_ERR_ALIAS;
+  if (overlap(rw, range_of(d->o, T * H * D * es)) ||
+      overlap(rw, range_of(d->ht, d->ht ? N * H * D * D * 4 : 0)))
+    return KDA_ERR_ALIAS;
   return hip_status(kda::launch_prefill(a, workspace, (hipStream_t)stream,
                                         reinterpret_cast<const hipEvent_t*>(events)));
 }
@@ -194,24 +225,28 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
     return KDA_ERR_SHAPE;
   if (d->dk != d->dv || !supported_d(d->dk)) return KDA_ERR_UNSUPPORTED;
   if (!std::isfinite(d->scale)) return KDA_ERR_SHAPE;
+  if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
   if (d->n_seqs == 0) return KDA_OK;
-  if (!d->state || !d->q || !d->k || !d->v || !d->g || !d->beta || !d->o) return KDA_ERR_NULL;
+  if (!d->state || !d->q || !d->k || !d->v || !d->beta || !d->o) return KDA_ERR_NULL;
   const bool bf = d->dtype == KDA_DTYPE_BF16;
   // the state is read and written as 16-byte vectors; the rest element-wise
-  if (!aligned(d->state, 16) || !aligned(d->g, 4)) return KDA_ERR_ALIGN;
+  if (!aligned(d->state, 16)) return KDA_ERR_ALIGN;
   const void* pe[] = {d->q, d->k, d->v, d->beta, d->o};
   for (const void* p : pe)
     if (!aligned(p, bf ? 2 : 4)) return KDA_ERR_ALIGN;
   const int64_t es = bf ? 2 : 4, NH = (int64_t)d->n_seqs * d->n_heads, D = d->dk;
+  kda::DecodeArgs a;
+  Range rgate[3];
+  const int st = check_gate(d->gate, d->g, true, d->n_seqs, d->n_heads, D, es, &a.gate, rgate);
+  if (st != KDA_OK) return st;
   const Range ro = range_of(d->o, NH * D * es);
   const Range ins[] = {range_of(d->state, NH * D * D * 4), range_of(d->q, NH * D * es),
                        range_of(d->k, NH * D * es),        range_of(d->v, NH * D * es),
-                       range_of(d->g, NH * D * 4),         range_of(d->beta, NH * es)};
+                       rgate[0], rgate[1], rgate[2],       range_of(d->beta, NH * es)};
   for (const Range& r : ins)
     if (overlap(ro, r)) return KDA_ERR_ALIAS;
-  for (int i = 1; i < 6; ++i)
+  for (int i = 1; i < 8; ++i)
     if (overlap(ins[0], ins[i])) return KDA_ERR_ALIAS;
-  kda::DecodeArgs a;
   a.bf16 = bf;
   a.n_seqs = d->n_seqs;
   a.n_heads = d->n_heads;

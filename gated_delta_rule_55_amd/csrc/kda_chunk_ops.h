@@ -39,7 +39,6 @@ __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t cmaxz(size_t a, size_t b) { return a > b ? a : b; }
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLocalThreads = 512;  // threads of a chunk-local workgroup (8 waves)
 constexpr float kSpanMax = 64.0f;  // largest log2 diagonal factor taken on the factored path
 
@@ -166,10 +165,21 @@ __device__ __forceinline__ float row_bcast(float x, int i) {
 
 // ---------------------------------------------------------------------------
 // Chunk-local stage.
-template <typename TIO, int D, int C>
+// The decay input of the chunk-local stage: g (fp32, natural log) when GATE
+// is false, else the raw gate x (TIO), a_log [H] and dt_bias [H, D].
+template <typename TIO>
+struct DecayIn {
+  const float* g;
+  const TIO* x;
+  const float* a_log;
+  const float* dt_bias;
+};
+
+template <typename TIO, int D, int C, bool GATE = false>
 struct ChunkLocal {
   using Gm = Geo<TIO, D, C>;
   using FragT = typename Frag<TIO>::type;
+  using V4 = typename Vec4<TIO>::type;
   static constexpr int TT = Gm::TT, DT = Gm::DT, KBD = Gm::KBD, KCP = Gm::KCP, KBC = Gm::KBC;
   static constexpr int GS_LD = Gm::GS_LD, KS_LD = Gm::KS_LD, TK_LD = Gm::TK_LD,
                        AF_LD = Gm::AF_LD;
@@ -187,7 +197,10 @@ struct ChunkLocal {
   // the loads in flight and never has to wait for the whole prefetch early.
   struct Inputs {
     uint4 k[NV], q[NV], v[NV];
-    f32x4 g[NG];
+    f32x4 g[GATE ? 1 : NG];     // g, four channels per vector
+    V4 x[GATE ? NG : 1];        // or the raw gate
+    f32x4 bias[GATE ? NG : 1];  // and dt_bias for the same channels
+    float ea;                   // exp(a_log[h])
     TIO beta;
     int64_t tok0;
     int len;
@@ -201,7 +214,7 @@ struct ChunkLocal {
   static __device__ __forceinline__ void prefetch(Inputs& in, const TIO* __restrict__ q,
                                                   const TIO* __restrict__ k,
                                                   const TIO* __restrict__ v,
-                                                  const float* __restrict__ g,
+                                                  const DecayIn<TIO>& dec,
                                                   const TIO* __restrict__ beta, int n_heads,
                                                   int h, int64_t tok0, int L) {
     const int tid = threadIdx.x;
@@ -223,8 +236,15 @@ struct ChunkLocal {
       const int x0 = tid + NT * m;
       const int x = x0 < C * GPR ? x0 : C * GPR - 1;
       const int r = min(x / GPR, L - 1), cv = x % GPR;
-      in.g[m] = reinterpret_cast<const f32x4*>(g + (tok0 + r) * rs + (int64_t)h * D)[cv];
+      const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
+      if constexpr (GATE) {
+        in.x[m] = reinterpret_cast<const V4*>(dec.x + off)[cv];
+        in.bias[m] = reinterpret_cast<const f32x4*>(dec.dt_bias + (int64_t)h * D)[cv];
+      } else {
+        in.g[m] = reinterpret_cast<const f32x4*>(dec.g + off)[cv];
+      }
     }
+    in.ea = GATE ? __expf(dec.a_log[h]) : 1.f;
     in.beta = beta[(tok0 + min(tid, L - 1)) * n_heads + h];
   }
 
@@ -233,7 +253,7 @@ struct ChunkLocal {
   // 16a + 4lg + j, column 16a + l16 (accumulator layout).
   static __device__ void exact_diag_tile(int a, f32x4& akk, f32x4& aqk,
                                          const TIO* __restrict__ q, const TIO* __restrict__ k,
-                                         const float* __restrict__ g, int n_heads, int h,
+                                         const DecayIn<TIO>& dec, float ea, int n_heads, int h,
                                          int64_t tok0, int L) {
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, lg = lane >> 4;
@@ -245,9 +265,15 @@ struct ChunkLocal {
       float sk = 0.f, sq = 0.f;
       if (ii <= rr && rr < L) {
         for (int c = 0; c < D; ++c) {
-          float e = 0.f;  // G[rr] - G[ii] = sum of g over (ii, rr]
-          for (int t = ii + 1; t <= rr; ++t) e += g[(tok0 + t) * rs + (int64_t)h * D + c];
-          const float f = fast_exp2(e * kLog2e);
+          float e = 0.f;  // G[rr] - G[ii] = log2(e) x (sum of g over (ii, rr])
+          for (int t = ii + 1; t <= rr; ++t) {
+            const int64_t at = (tok0 + t) * rs + (int64_t)h * D + c;
+            if constexpr (GATE)
+              e += kimi_gate_log2(to_f32(dec.x[at]) + dec.dt_bias[(int64_t)h * D + c], ea);
+            else
+              e += dec.g[at] * kLog2e;
+          }
+          const float f = fast_exp2(e);
           const float ki = to_f32(k[(tok0 + ii) * rs + (int64_t)h * D + c]) * f;
           sk += to_f32(k[(tok0 + rr) * rs + (int64_t)h * D + c]) * ki;
           sq += to_f32(q[(tok0 + rr) * rs + (int64_t)h * D + c]) * ki;
@@ -285,7 +311,7 @@ struct ChunkLocal {
   // (chunk, head); run() never waits on global memory otherwise.
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
                              ChunkOut<TIO> out, const TIO* __restrict__ q,
-                             const TIO* __restrict__ k, const float* __restrict__ g, int n_heads,
+                             const TIO* __restrict__ k, const DecayIn<TIO>& dec, int n_heads,
                              int h) {
     float* Gs = reinterpret_cast<float*>(lds + Gm::OFF_GS);
     float* As = reinterpret_cast<float*>(lds + Gm::OFF_AS);
@@ -335,7 +361,13 @@ struct ChunkLocal {
       if (x < C * GPR) {
         const int r = x / GPR, cv = x % GPR;
         const bool live = r < in.len;
-        f32x4 gv = in.g[m] * kLog2e;
+        f32x4 gv;
+        if constexpr (GATE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gv[e] = kimi_gate_log2(to_f32(in.x[m][e]) + in.bias[m][e], in.ea);
+        } else {
+          gv = in.g[m] * kLog2e;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) gv[e] = live ? gv[e] : 0.f;
         *reinterpret_cast<f32x4*>(Gs + r * GS_LD + 4 * cv) = gv;
@@ -460,7 +492,7 @@ struct ChunkLocal {
         }
         f32x4 akk = zero4(), aqk = zero4();
         if (a == b && (flag >> a) & 1) {
-          exact_diag_tile(a, akk, aqk, q, k, g, n_heads, h, in.tok0, in.len);
+          exact_diag_tile(a, akk, aqk, q, k, dec, in.ea, n_heads, h, in.tok0, in.len);
         } else {
           const TIO* lkr = Lk + (16 * a + l16) * KS_LD;
           const TIO* lqr = Lq + (16 * a + l16) * KS_LD;

@@ -23,13 +23,18 @@
 
 namespace kda {
 
-template <typename TIO, int D>
+// GATE: the decay comes from the raw gate x with a_log and dt_bias (the Kimi
+// gate, see kimi_gate_log2) instead of a given g.
+template <typename TIO, int D, bool GATE>
 __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
                                                      const TIO* __restrict__ q,
                                                      const TIO* __restrict__ k,
                                                      const TIO* __restrict__ v,
                                                      const float* __restrict__ g,
-                                                     const TIO* __restrict__ beta,
+                                                     const TIO* __restrict__ gx,
+                                                     const float* __restrict__ a_log,
+                                                     const float* __restrict__ dt_bias,
+                                                     int n_heads, const TIO* __restrict__ beta,
                                                      TIO* __restrict__ o, float scale) {
   constexpr int NQ = D / 4;       // column quads per row
   constexpr int RG = 256 / NQ;    // row groups
@@ -55,7 +60,13 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   if (tid < D) {
     s_q[tid] = to_f32(q[nh * D + tid]);
     s_k[tid] = to_f32(k[nh * D + tid]);
-    s_d[tid] = __expf(g[nh * D + tid]);
+    if constexpr (GATE) {
+      const int h = (int)(nh % n_heads);
+      s_d[tid] = fast_exp2(kimi_gate_log2(to_f32(gx[nh * D + tid]) + dt_bias[h * D + tid],
+                                          __expf(a_log[h])));
+    } else {
+      s_d[tid] = __expf(g[nh * D + tid]);
+    }
   }
   __syncthreads();
   if (tid < 64) {  // k . q by one wave
@@ -103,9 +114,16 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 template <typename TIO, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
-  hipLaunchKernelGGL((decode_kernel<TIO, D>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                     a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
-                     (const TIO*)a.beta, (TIO*)a.o, a.scale);
+  if (a.gate.mode == GATE_KIMI_)
+    hipLaunchKernelGGL((decode_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                       a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
+                       (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias, a.n_heads,
+                       (const TIO*)a.beta, (TIO*)a.o, a.scale);
+  else
+    hipLaunchKernelGGL((decode_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0, stream,
+                       a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
+                       (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
+                       a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale);
   return hipGetLastError();
 }
 

@@ -129,6 +129,31 @@ __device__ __forceinline__ typename Frag<T>::type frag_from_d(f32x4 d0, f32x4 d1
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The Kimi gate in base 2: g log2(e) with g = -exp(a_log) softplus(z),
+// z = x + dt_bias, given ea = exp(a_log).  softplus(z) log2(e) =
+// log2(1 + 2^(z log2 e)), which is z log2(e) to fp32 precision once that
+// exceeds 24.  (For very negative z, 1 + 2^(z log2 e) rounds to 1 and the
+// gate reads 0 instead of a value below 1e-7 of ea: no decay lost that fp32
+// could hold.)
+__device__ __forceinline__ float kimi_gate_log2(float z, float ea) {
+  const float zl = z * kLog2e;
+  return -ea * (zl > 24.f ? zl : __builtin_amdgcn_logf(1.f + fast_exp2(zl)));
+}
+
+// Four values of T in one vector (8 bytes for bf16, 16 for fp32).
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<bf16> {
+  typedef bf16x4 type;
+};
+template <>
+struct Vec4<float> {
+  typedef f32x4 type;
+};
+
 // Raw buffer stores: a lane whose byte offset is at or past the buffer's
 // num_records has its store dropped by the hardware, so a masked store needs
 // no branch.  kBufferOff is such an offset.

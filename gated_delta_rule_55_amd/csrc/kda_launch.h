@@ -8,6 +8,18 @@
 
 namespace kda {
 
+// Decay input: g given (GATE_GIVEN_), or computed in the kernels from the raw
+// gate x, a_log [H] and dt_bias [H, d] (GATE_KIMI_); values as kda_gate.
+constexpr int GATE_GIVEN_ = 0;
+constexpr int GATE_KIMI_ = 1;
+
+struct GateArgs {
+  int mode = GATE_GIVEN_;
+  const void* x = nullptr;  // dtype of q
+  const float* a_log = nullptr;
+  const float* dt_bias = nullptr;
+};
+
 struct DecodeArgs {
   bool bf16;
   int n_seqs, n_heads, d;
@@ -17,6 +29,7 @@ struct DecodeArgs {
   const float* g;
   const void* beta;
   void* o;
+  GateArgs gate;
 };
 
 // Launch plans (same values as kda_plan in include/kda.h).
@@ -36,6 +49,7 @@ struct PrefillArgs {
   const int32_t* cu_seqlens;  // may be NULL when n_seqs == 1
   void* o;
   float* ht;
+  GateArgs gate;
 };
 
 // Upper bound on the number of chunks: sum_n ceil(L_n / C) <= T / C + N.

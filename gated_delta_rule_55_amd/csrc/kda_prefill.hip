@@ -159,23 +159,23 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 // Two-pass plan, stage 1: chunk-local stage for every (chunk, head).  A
 // persistent grid (one workgroup per CU) walks the (chunk, head) items; the
 // next item's inputs are loaded while the current one computes.
-template <typename TIO, int D, int C>
+template <typename TIO, int D, int C, bool GATE>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
-    const float* __restrict__ g, const TIO* __restrict__ beta, int n_heads, float scale,
+    DecayIn<TIO> dec, const TIO* __restrict__ beta, int n_heads, float scale,
     const int* __restrict__ chunk_total, const ChunkEnt* __restrict__ tab,
     unsigned char* __restrict__ blocks) {
-  using CL = ChunkLocal<TIO, D, C>;
+  using CL = ChunkLocal<TIO, D, C, GATE>;
   using Gm = Geo<TIO, D, C>;
   extern __shared__ __align__(16) unsigned char lds[];
   const int n_items = *chunk_total * n_heads;
   auto fetch = [&](typename CL::Inputs& in, int w) {
     const ChunkEnt ent = tab[w / n_heads];
-    CL::prefetch(in, q, k, v, g, beta, n_heads, w % n_heads, ent.start, ent.len);
+    CL::prefetch(in, q, k, v, dec, beta, n_heads, w % n_heads, ent.start, ent.len);
   };
   auto compute = [&](const typename CL::Inputs& in, int w) {
     const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)w * Gm::OUT_BYTES);
-    CL::run(lds, in, scale, out, q, k, g, n_heads, w % n_heads);
+    CL::run(lds, in, scale, out, q, k, dec, n_heads, w % n_heads);
     __syncthreads();  // the next item overwrites the LDS
   };
   typename CL::Inputs cur, nxt;
@@ -360,6 +360,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
   const TIO* v = static_cast<const TIO*>(a.v);
   const TIO* beta = static_cast<const TIO*>(a.beta);
   TIO* o = static_cast<TIO*>(a.o);
+  const DecayIn<TIO> dec{a.g, nullptr, nullptr, nullptr};
 
   // team / member, XCD-aware: members of a team share blockIdx mod 8
   const int G = gridDim.x;
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
     have_in = !pc.end;
     if (have_in) {
       const ChunkEnt ent = a.tab[pc.ci];
-      CL::prefetch(in, q, k, v, a.g, beta, a.n_heads, pc.h, ent.start, ent.len);
+      CL::prefetch(in, q, k, v, dec, beta, a.n_heads, pc.h, ent.start, ent.len);
     }
   };
   // Produce chunk ps from `in`, publish it, step to this member's next chunk
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
       if (!s_ok) return false;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    CL::run(lds, in, a.scale, slot_out(ps), q, k, a.g, a.n_heads, pc.h);
+    CL::run(lds, in, a.scale, slot_out(ps), q, k, dec, a.n_heads, pc.h);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // every wave's stores
     __syncthreads();
     if (tid == 0)
@@ -590,8 +591,11 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
     }
 
     unsigned char* blocks = ws + L.off_blocks;
-    err = hipFuncSetAttribute((const void*)chunk_local_kernel<TIO, D, C>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)Gm::LOCAL_LDS);
+    const bool gate = a.gate.mode == GATE_KIMI_;
+    const void* local_fn = gate ? (const void*)chunk_local_kernel<TIO, D, C, true>
+                                : (const void*)chunk_local_kernel<TIO, D, C, false>;
+    err = hipFuncSetAttribute(local_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)Gm::LOCAL_LDS);
     if (err != hipSuccess) return err;
     int dev = 0, cus = 0;
     if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
@@ -600,10 +604,18 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
       return err;
     const int64_t items = ntu * a.n_heads;
     const unsigned grid = (unsigned)(items < cus ? items : cus);
-    hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C>), dim3(grid), dim3(kLocalThreads),
-                       Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
-                       (const TIO*)a.v, a.g, (const TIO*)a.beta, a.n_heads, a.scale,
-                       chunk_off + a.n_seqs, tab, blocks);
+    const DecayIn<TIO> dec{a.g, static_cast<const TIO*>(a.gate.x), a.gate.a_log,
+                           a.gate.dt_bias};
+    if (gate)
+      hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, true>), dim3(grid), dim3(kLocalThreads),
+                         Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
+                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads, a.scale,
+                         chunk_off + a.n_seqs, tab, blocks);
+    else
+      hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, false>), dim3(grid), dim3(kLocalThreads),
+                         Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
+                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads, a.scale,
+                         chunk_off + a.n_seqs, tab, blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
     const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * (D / 16));

@@ -40,8 +40,31 @@ _PLANS = {"auto": _abi.KDA_PLAN_AUTO, "fused": _abi.KDA_PLAN_FUSED,
           "two_pass": _abi.KDA_PLAN_TWO_PASS}
 
 
+def _gate_tuple(gate):
+    if gate is None:
+        return (_abi.KDA_GATE_GIVEN, None, None, None)
+    x, a_log, dt_bias = gate
+    return (_abi.KDA_GATE_KIMI, _ptr(x), _ptr(a_log), _ptr(dt_bias))
+
+
+def _check_gate(gate, g, lead, H, dk, dtype, dev):
+    """g [*lead, H, dk] fp32, or gate = (x [*lead, H, dk] in dtype, a_log [H]
+    fp32, dt_bias [H, dk] fp32)."""
+    if gate is None:
+        if g is None:
+            raise ValueError("g is required unless gate = (x, a_log, dt_bias) is given")
+        _check(g, "g", (*lead, H, dk), torch.float32, dev)
+        return
+    if len(gate) != 3:
+        raise ValueError("gate must be (x, a_log, dt_bias)")
+    x, a_log, dt_bias = gate
+    _check(x, "gate x", (*lead, H, dk), dtype, dev)
+    _check(a_log, "gate a_log", (H,), torch.float32, dev)
+    _check(dt_bias, "gate dt_bias", (H, dk), torch.float32, dev)
+
+
 def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
-                 ht=None, plan="auto") -> _abi.PrefillDesc:
+                 ht=None, plan="auto", gate=None) -> _abi.PrefillDesc:
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
@@ -49,7 +72,7 @@ def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=6
         dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv, chunk=int(chunk),
         plan=_PLANS[plan], t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
         v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
-        o=_ptr(o), ht=_ptr(ht))
+        o=_ptr(o), ht=_ptr(ht), gate=_gate_tuple(gate))
 
 
 def prefill_workspace_bytes(T: int, H: int, d: int, n_seqs: int = 1, chunk: int = 64,
@@ -59,13 +82,13 @@ def prefill_workspace_bytes(T: int, H: int, d: int, n_seqs: int = 1, chunk: int 
     return _abi.workspace_bytes(desc)
 
 
-def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
                   beta: torch.Tensor, h0: Optional[torch.Tensor] = None,
                   cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                   chunk: int = 64, out: Optional[torch.Tensor] = None,
                   ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   output_final_state: bool = True, stream=None, events=None,
-                  plan: str = "auto") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  plan: str = "auto", gate=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
     h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
     None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
@@ -73,7 +96,10 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     objects recorded before the first launch and after each of the three
     launches (chunk map, chunk-local stage, state scan), for stage timing (the
     fused plan has one launch after the chunk map; its time is reported as the
-    chunk-local stage).  `plan`: "auto", "fused" or "two_pass"."""
+    chunk-local stage).  `plan`: "auto", "fused" or "two_pass".  `gate`: None
+    (g given), or (x [T, H, dk] in q's dtype, a_log [H] fp32, dt_bias [H, dk]
+    fp32) to compute g = -exp(a_log) softplus(x + dt_bias) in the kernels
+    (g may then be None)."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("chunk_prefill runs on the GPU only")
@@ -84,7 +110,7 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
     _check(k, "k", (T, H, dk), q.dtype, dev)
     _check(v, "v", (T, H, dv), q.dtype, dev)
-    _check(g, "g", (T, H, dk), torch.float32, dev)
+    _check_gate(gate, g, (T,), H, dk, q.dtype, dev)
     _check(beta, "beta", (T, H), q.dtype, dev)
     _check(q, "q", (T, H, dk), q.dtype, dev)
     if h0 is not None:
@@ -99,7 +125,7 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif ht is not None:
         _check(ht, "ht", (N, H, dk, dv), torch.float32, dev)
-    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan)
+    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate)
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -113,10 +139,11 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
 
 
 def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                     g: torch.Tensor, beta: torch.Tensor, scale: Optional[float] = None,
-                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                     g: Optional[torch.Tensor], beta: torch.Tensor, scale: Optional[float] = None,
+                     out: Optional[torch.Tensor] = None, stream=None, gate=None) -> torch.Tensor:
     """One recurrent decode step; `state` [N, H, dk, dv] fp32 is updated in place.
-    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].  Returns o [N, H, dv]."""
+    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].  Returns o [N, H, dv].
+    `gate` as in chunk_prefill (x is [N, H, dk])."""
     dev = state.device
     if dev.type != "cuda":
         raise ValueError("recurrent_decode runs on the GPU only")
@@ -127,7 +154,7 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     _check(q, "q", (N, H, dk), q.dtype, dev)
     _check(k, "k", (N, H, dk), q.dtype, dev)
     _check(v, "v", (N, H, dv), q.dtype, dev)
-    _check(g, "g", (N, H, dk), torch.float32, dev)
+    _check_gate(gate, g, (N,), H, dk, q.dtype, dev)
     _check(beta, "beta", (N, H), q.dtype, dev)
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
@@ -135,8 +162,8 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
         _check(out, "out", (N, H, dv), q.dtype, dev)
     desc = _abi.decode_desc(dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv,
                             scale=0.0 if scale is None else float(scale), state=state.data_ptr(),
-                            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=g.data_ptr(),
-                            beta=beta.data_ptr(), o=out.data_ptr())
+                            q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=_ptr(g),
+                            beta=beta.data_ptr(), o=out.data_ptr(), gate=_gate_tuple(gate))
     st = _abi.recurrent_decode_raw(desc, _stream(stream))
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_recurrent_decode")

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -72,6 +72,24 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_DTYPE_F32 = 1, KDA_DTYPE_BF16 = 2 } kda_dtype;
+
+/* Decay input.  GIVEN: the caller passes g, the natural-log decay, fp32.
+ * KIMI: the gate activation is computed inside the kernels from the raw gate
+ * x (dtype of q), a per-head a_log [H] and a per-(head, channel) dt_bias
+ * [H, dk], both fp32:  g = -exp(a_log[h]) * softplus(x + dt_bias[h, c]),
+ * softplus(z) = log(1 + e^z).  The pages run this activation fused into the
+ * chunked forward (page "spike(kimi-linear): chunk_kda prefill AOT port",
+ * commit message: the gate/cumsum kernel of chunk_kda_with_fused_gate); the
+ * formula is the Kimi-Linear gate of the workload definition.  Fusing it
+ * means the kernels read x in the input dtype instead of an fp32 g. */
+typedef enum { KDA_GATE_GIVEN = 0, KDA_GATE_KIMI = 1 } kda_gate;
+
+typedef struct {
+  int32_t mode;               /* kda_gate; 0 = g given                          */
+  const void* x;              /* KIMI: raw gate [.., H, dk], dtype of q         */
+  const float* a_log;         /* KIMI: [H] fp32                                 */
+  const float* dt_bias;       /* KIMI: [H, dk] fp32                             */
+} kda_gate_desc;
 
 /* Launch plan of the chunked prefill.  TWO_PASS writes the chunk-local
  * results to the workspace and reads them back in the state scan; AUTO
@@ -121,6 +139,8 @@ typedef struct {
   const int32_t* cu_seqlens;  /* NULL allowed when n_seqs == 1                  */
   void* o;
   float* ht;                  /* NULL = final state not returned               */
+  kda_gate_desc gate;         /* g, or the raw gate and its parameters; g may  */
+                              /* be NULL when gate.mode = KIMI                 */
 } kda_prefill_desc;
 
 /* One recurrent decode step for a batch of N sequences, one token each.
@@ -140,6 +160,7 @@ typedef struct {
   const float* g;
   const void* beta;
   void* o;
+  kda_gate_desc gate;         /* as in kda_prefill_desc; x is [N, H, dk]        */
 } kda_decode_desc;
 
 /* KDA_ABI_VERSION of the loaded library. */

@@ -96,6 +96,13 @@ class KdaInputs:
     chunk: int = 64
     scale: float = 0.0
     meta: dict = field(default_factory=dict)
+    # The raw gate behind g, for the fused-gate path: x [T, H, dk] rounded to
+    # the storage dtype, a_log [H] and dt_bias [H, dk] rounded to fp32 ("softplus"
+    # gates have a_log = 0 and dt_bias = 0).  g above was made from the
+    # unrounded values; a fused-gate reference recomputes it from these.
+    gate_x: Optional[np.ndarray] = None
+    gate_a_log: Optional[np.ndarray] = None
+    gate_dt_bias: Optional[np.ndarray] = None
 
     @property
     def T(self) -> int:
@@ -116,6 +123,11 @@ class KdaInputs:
     @property
     def N(self) -> int:
         return int(self.cu_seqlens.shape[0] - 1)
+
+    def gate_f64(self) -> tuple:
+        """(x, a_log, dt_bias) of the raw gate as stored, widened to fp64."""
+        return (_widen(self.gate_x, self.dtype), np.asarray(self.gate_a_log, dtype=np.float64),
+                np.asarray(self.gate_dt_bias, dtype=np.float64))
 
     def f64(self) -> dict:
         """The same values widened to fp64, as the oracle consumes them."""
@@ -168,6 +180,8 @@ def make_inputs(
     def draw_g():
         x = _rng(seed, "x").standard_normal((T, H, dk))
         if gate == "softplus":
+            a = np.zeros(H)
+            b = np.zeros((H, dk))
             g = -_softplus(x)
         elif gate == "kimi":
             a = _rng(seed, "a").uniform(-3.0, 0.0, size=(H,))
@@ -175,13 +189,14 @@ def make_inputs(
             g = -np.exp(a)[None, :, None] * _softplus(x + b[None, :, :])
         else:
             raise ValueError(f"unknown gate {gate!r}")
-        return np.ascontiguousarray(g.astype(np.float32))
+        return (np.ascontiguousarray(g.astype(np.float32)), _store(x, dtype),
+                a.astype(np.float32), np.ascontiguousarray(b.astype(np.float32)))
 
     if gate not in ("softplus", "kimi"):
         raise ValueError(f"unknown gate {gate!r}")
     with ThreadPoolExecutor(max_workers=4) as pool:
         futs = [pool.submit(f) for f in (draw_q, draw_k, draw_v, draw_g)]
-        q_s, k_s, v_s, g_s = (f.result() for f in futs)
+        q_s, k_s, v_s, (g_s, x_s, a_s, b_s) = (f.result() for f in futs)
     beta = 1.0 / (1.0 + np.exp(-_rng(seed, "beta").standard_normal((T, H))))
     h0 = None
     if h0_std > 0.0:
@@ -198,6 +213,9 @@ def make_inputs(
         chunk=chunk,
         scale=float(dk ** -0.5) if scale is None else float(scale),
         meta={"seed": seed, "lengths": lengths, "gate": gate, "h0_std": h0_std},
+        gate_x=x_s,
+        gate_a_log=a_s,
+        gate_dt_bias=b_s,
     )
 
 
@@ -256,4 +274,7 @@ def slice_heads(inp: KdaInputs, heads: Sequence[int]) -> KdaInputs:
         chunk=inp.chunk,
         scale=inp.scale,
         meta=dict(inp.meta, heads=[int(h) for h in hs]),
+        gate_x=None if inp.gate_x is None else np.ascontiguousarray(inp.gate_x[:, hs]),
+        gate_a_log=None if inp.gate_a_log is None else inp.gate_a_log[hs].copy(),
+        gate_dt_bias=None if inp.gate_dt_bias is None else np.ascontiguousarray(inp.gate_dt_bias[hs]),
     )

@@ -40,9 +40,18 @@ def dev_inputs(inp: synth.KdaInputs, dev="cuda") -> dict:
     }
 
 
-def oracle_prefill(inp: synth.KdaInputs):
+def dev_gate(inp: synth.KdaInputs, dev="cuda") -> tuple:
+    """The raw gate (x, a_log, dt_bias) on the device, as the fused-gate path takes it."""
+    return (to_dev(inp.gate_x, inp.dtype, dev), to_dev(inp.gate_a_log, "f32", dev),
+            to_dev(inp.gate_dt_bias, "f32", dev))
+
+
+def oracle_prefill(inp: synth.KdaInputs, fused_gate: bool = False):
+    """fp64 oracle on the rounded inputs; with fused_gate, g is recomputed by
+    the oracle from the stored raw gate (what the fused-gate path receives)."""
     f = inp.f64()
-    return oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"], f["cu_seqlens"],
+    g = oracle.kimi_gate(*inp.gate_f64()) if fused_gate else f["g"]
+    return oracle.prefill(f["q"], f["k"], f["v"], g, f["beta"], f["h0"], f["cu_seqlens"],
                           f["scale"])
 
 

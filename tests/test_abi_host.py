@@ -115,6 +115,41 @@ def test_prefill_rejects_bad_pointers(abi, over, status):
 
 
 @no_gpu_only
+@pytest.mark.parametrize("gate,g,status", [
+    ((5, 0x800000, 0x900000, 0xa00000), 0x400000, -4),        # unknown mode
+    ((1, None, 0x900000, 0xa00000), None, -1),                 # KIMI without x
+    ((1, 0x800000, None, 0xa00000), None, -1),                 # KIMI without a_log
+    ((1, 0x800001, 0x900000, 0xa00000), None, -5),             # x misaligned (bf16)
+    ((1, 0x800000, 0x900002, 0xa00000), None, -5),             # a_log misaligned
+    ((1, 0x600000 + 64, 0x900000, 0xa00000), None, -9),        # x overlaps o
+    ((0, None, None, None), None, -1),                         # GIVEN without g
+])
+def test_prefill_gate_validation(abi, gate, g, status):
+    d = _valid_prefill(abi, gate=gate, g=g)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == status
+
+
+@no_gpu_only
+def test_prefill_gate_kimi_needs_no_g(abi):
+    """With the gate computed in the kernels, g may be NULL: every pointer check
+    passes and the call stops at the (too small) workspace."""
+    d = _valid_prefill(abi, gate=(1, 0x800000, 0x900000, 0xa00000), g=None)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 16, 0) == abi.KDA_ERR_WORKSPACE
+
+
+@no_gpu_only
+def test_decode_gate_validation(abi):
+    kw = dict(dtype=abi.KDA_DTYPE_BF16, n_seqs=2, n_heads=2, dk=64, dv=64, state=0x100000,
+              q=0x900000, k=0xa00000, v=0xb00000, g=None, beta=0xd00000, o=0xe00000)
+    d = abi.decode_desc(**kw, gate=(1, None, 0x700000, 0x780000))
+    assert abi.recurrent_decode_raw(d, 0) == abi.KDA_ERR_NULL
+    d = abi.decode_desc(**kw, gate=(3, 0x600000, 0x700000, 0x780000))
+    assert abi.recurrent_decode_raw(d, 0) == abi.KDA_ERR_UNSUPPORTED
+    d = abi.decode_desc(**kw, gate=(1, 0xe00000, 0x700000, 0x780000))  # x is o
+    assert abi.recurrent_decode_raw(d, 0) == abi.KDA_ERR_ALIAS
+
+
+@no_gpu_only
 def test_fused_plan_is_switched_off(abi):
     """A fused-plan request is refused on the host, before any launch."""
     d = _valid_prefill(abi, plan=abi.KDA_PLAN_FUSED)
