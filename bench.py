@@ -177,7 +177,48 @@ def bench_decode(args, torch, kda, synth):
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b))
     ms = statistics.median(times)
-    return inp, S, ms, dec
+    rec = bench_recurrent(args, torch, kda, inp, state0, dec, stream)
+    return inp, S, ms, dec, rec
+
+
+def bench_recurrent(args, torch, kda, inp, state0, dec, stream, R=16):
+    """Continuing prefill: the next R tokens of all 64 sequences in one
+    recurrent-prefill call on the carried state (a state pool, slot n for
+    sequence n), against R decode steps doing the same work."""
+    N, H, D = state0.shape[0], inp.H, inp.dk
+    packed = {kk: t[:R].transpose(0, 1).reshape(N * R, *t.shape[2:]).contiguous()
+              for kk, t in dec.items()}
+    cu = torch.arange(0, N * R + 1, R, dtype=torch.int32, device="cuda")
+    slots = torch.arange(N, dtype=torch.int32, device="cuda")
+    pool = state0.clone()
+    out = torch.empty((N * R, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        kda.recurrent_prefill(packed["q"], packed["k"], packed["v"], packed["g"], packed["beta"],
+                              pool, cu, scale=inp.scale, out=out, ht=pool, state_indices=slots)
+
+    call()  # warm-up
+    times = []
+    for _ in range(max(3, args.decode_reps)):
+        pool.copy_(state0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = statistics.median(times)
+    rbytes = DECODE_STATE_BYTES + R * DECODE_TOKEN_BYTES
+    ach = rbytes / (ms / 1e3) / 1e9
+    return {"workload": f"continuing prefill: {R} new tokens for each of 64 sequences (H=32, "
+                        "d=128) on the carried decode-leg state, one recurrent-prefill call "
+                        "over a 64-slot state pool",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(N * R / (ms / 1e3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "scope": f"state read + write once and {R} tokens' inputs and outputs, "
+                                  f"{rbytes} bytes per call"}}
 
 
 def cpu_prefill_baseline(args, inp):
@@ -293,7 +334,7 @@ def main():
             "kernels_ms": {kname: round(v, 4) for kname, v in gstage.items()},
         }
     if not args.no_decode:
-        dinp, S, dms, dec = bench_decode(args, torch, kda, synth)
+        dinp, S, dms, dec, rec = bench_decode(args, torch, kda, synth)
         step_ms = dms / S
         dbytes = DECODE_STATE_BYTES + DECODE_TOKEN_BYTES
         dach = dbytes / (step_ms / 1e3) / 1e9
@@ -307,6 +348,7 @@ def main():
                          "traffic": measured_traffic("decode"),
                          "note": "the 134 MB state fits the 256 MB Infinity Cache"},
         }
+        line["recurrent_prefill"] = rec
         if not args.no_cpu:
             log("timing the CPU oracle (decode)")
             line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)

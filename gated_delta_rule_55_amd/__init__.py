@@ -4,6 +4,7 @@ from .kda import (  # noqa: F401
     chunk_prefill,
     prefill_workspace_bytes,
     recurrent_decode,
+    recurrent_prefill,
     workspace_status,
 )
 from ._abi import KdaError, LIB_PATH  # noqa: F401

@@ -64,6 +64,8 @@ class PrefillDesc(ctypes.Structure):
         ("o", ctypes.c_void_p),
         ("ht", ctypes.c_void_p),
         ("gate", GateDesc),
+        ("state_indices", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int32),
     ]
 
 
@@ -84,6 +86,8 @@ class DecodeDesc(ctypes.Structure):
         ("beta", ctypes.c_void_p),
         ("o", ctypes.c_void_p),
         ("gate", GateDesc),
+        ("state_indices", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int32),
     ]
 
 
@@ -126,6 +130,8 @@ def lib():
         L.kda_workspace_status.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.c_void_p]
         L.kda_recurrent_decode.restype = ctypes.c_int
+        L.kda_recurrent_prefill.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p]
+        L.kda_recurrent_prefill.restype = ctypes.c_int
         if L.kda_abi_version() != KDA_ABI_VERSION:
             raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != {KDA_ABI_VERSION}")
         _LIB = L
@@ -182,6 +188,10 @@ def chunk_prefill_timed_raw(desc: PrefillDesc, workspace: int, workspace_bytes: 
 
 def recurrent_decode_raw(desc: DecodeDesc, stream: int) -> int:
     return int(lib().kda_recurrent_decode(ctypes.byref(desc), stream))
+
+
+def recurrent_prefill_raw(desc: PrefillDesc, stream: int) -> int:
+    return int(lib().kda_recurrent_prefill(ctypes.byref(desc), stream))
 
 
 def workspace_status(workspace: int, stream: int) -> int:

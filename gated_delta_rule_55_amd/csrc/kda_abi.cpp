@@ -67,7 +67,9 @@ int check_gate(const kda_gate_desc& gt, const float* g, bool work, int64_t rows,
 }
 
 // Shared checks of the prefill descriptor; fills `a` on success.
-int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
+// chunked: the chunked prefill (chunk and plan are checked); else the
+// recurrent prefill, which ignores them.
+int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked = true) {
   if (!d) return KDA_ERR_NULL;
   if (d->struct_size != sizeof(kda_prefill_desc)) return KDA_ERR_VERSION;
   if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE;
@@ -75,17 +77,22 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
       d->t_total > INT32_MAX - 64)
     return KDA_ERR_SHAPE;
   if (d->dk != d->dv || !supported_d(d->dk)) return KDA_ERR_UNSUPPORTED;
+  if (d->state_indices && d->n_slots < 1) return KDA_ERR_SHAPE;
   const int chunk = d->chunk == 0 ? 64 : d->chunk;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
-  if (!kda::prefill_supported(d->dtype == KDA_DTYPE_BF16, d->dk, chunk)) return KDA_ERR_UNSUPPORTED;
+  if (chunked) {
+    if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (!kda::prefill_supported(d->dtype == KDA_DTYPE_BF16, d->dk, chunk))
+      return KDA_ERR_UNSUPPORTED;
+  }
   if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
-  if (d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
+  if (chunked &&
+      d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
     return KDA_ERR_UNSUPPORTED;
   if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
   // The fused plan is switched off: its workgroups wait on each other, and a
   // run of it left a GPU unusable without an explained cause.  It stays
   // rejected here, before anything is launched, until that is understood.
-  if (d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
+  if (chunked && d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
   a->plan = d->plan;
   a->n_seqs = d->n_seqs;
@@ -103,12 +110,14 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a) {
   a->cu_seqlens = d->cu_seqlens;
   a->o = d->o;
   a->ht = d->ht;
+  a->slots = d->state_indices;
+  a->n_slots = d->state_indices ? d->n_slots : 0;
   return KDA_OK;
 }
 
 // Checks the pointers; on success `rin` holds every input range the call
-// reads (q, k, v, the decay input (3), beta, h0, cu_seqlens).
-int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range (&rin)[9]) {
+// reads (q, k, v, the decay input (3), beta, h0, cu_seqlens, state_indices).
+int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range (&rin)[10]) {
   if (!d->cu_seqlens && d->n_seqs != 1) return KDA_ERR_NULL;
   if (d->t_total > 0 && (!d->q || !d->k || !d->v || !d->beta || !d->o)) return KDA_ERR_NULL;
   // q and k rows are read as 16-byte vectors; everything else element-wise.
@@ -117,12 +126,14 @@ int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range
   const void* pe[] = {d->v, d->beta, d->o};
   for (const void* p : pe)
     if (p && !aligned(p, es_al)) return KDA_ERR_ALIGN;
-  const void* p4[] = {d->h0, d->ht, d->cu_seqlens};
+  const void* p4[] = {d->h0, d->ht, d->cu_seqlens, d->state_indices};
   for (const void* p : p4)
     if (p && !aligned(p, 4)) return KDA_ERR_ALIGN;
 
   const int64_t es = a->bf16 ? 2 : 4;
-  const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
+  const int64_t T = d->t_total, H = d->n_heads, D = d->dk;
+  // h0 / ht hold N states, or n_slots with a slot table
+  const int64_t N = d->state_indices ? d->n_slots : d->n_seqs;
   Range rgate[3];
   const int st = check_gate(d->gate, d->g, T > 0, T, H, D, es, &a->gate, rgate);
   if (st != KDA_OK) return st;
@@ -131,9 +142,10 @@ int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range
               ro = range_of(d->o, T * H * D * es),
               rh0 = range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
               rht = range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
-              rcu = range_of(d->cu_seqlens, d->cu_seqlens ? (N + 1) * 4 : 0);
-  const Range inputs[9] = {rq, rk, rv, rgate[0], rgate[1], rgate[2], rb, rh0, rcu};
-  for (int i = 0; i < 9; ++i) rin[i] = inputs[i];
+              rcu = range_of(d->cu_seqlens, d->cu_seqlens ? ((int64_t)d->n_seqs + 1) * 4 : 0),
+              rsi = range_of(d->state_indices, d->state_indices ? (int64_t)d->n_seqs * 4 : 0);
+  const Range inputs[10] = {rq, rk, rv, rgate[0], rgate[1], rgate[2], rb, rh0, rcu, rsi};
+  for (int i = 0; i < 10; ++i) rin[i] = inputs[i];
   for (const Range& r : inputs)
     if (overlap(ro, r)) return KDA_ERR_ALIAS;
   if (overlap(ro, rht)) return KDA_ERR_ALIAS;
@@ -184,7 +196,7 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
   kda::PrefillArgs a;
   int st = check_prefill(d, &a);
   if (st != KDA_OK) return st;
-  Range rin[9];
+  Range rin[10];
   st = check_prefill_pointers(d, &a, rin);
   if (st != KDA_OK) return st;
   const size_t need = kda::prefill_workspace_bytes(a);
@@ -192,7 +204,8 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
   if (!aligned(workspace, 256)) return KDA_ERR_ALIGN;
   const Range rw = range_of(workspace, (int64_t)need);
   const int64_t es = a.bf16 ? 2 : 4;
-  const int64_t T = d->t_total, H = d->n_heads, D = d->dk, N = d->n_seqs;
+  const int64_t T = d->t_total, H = d->n_heads, D = d->dk;
+  const int64_t N = d->state_indices ? d->n_slots : d->n_seqs;
   for (const Range& r : rin)
     if (overlap(rw, r)) return KDA_ERR_ALIAS;
   if (overlap(rw, range_of(d->o, T * H * D * es)) ||
@@ -205,6 +218,16 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
 int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspace_bytes,
                       void* stream) {
   return kda_chunk_prefill_timed(d, workspace, workspace_bytes, stream, nullptr);
+}
+
+int kda_recurrent_prefill(const kda_prefill_desc* d, void* stream) {
+  kda::PrefillArgs a;
+  int st = check_prefill(d, &a, false);
+  if (st != KDA_OK) return st;
+  Range rin[10];
+  st = check_prefill_pointers(d, &a, rin);
+  if (st != KDA_OK) return st;
+  return hip_status(kda::launch_recurrent(a, (hipStream_t)stream));
 }
 
 int kda_workspace_status(const void* workspace, void* stream) {
@@ -226,11 +249,13 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   if (d->dk != d->dv || !supported_d(d->dk)) return KDA_ERR_UNSUPPORTED;
   if (!std::isfinite(d->scale)) return KDA_ERR_SHAPE;
   if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
+  if (d->state_indices && d->n_slots < 1) return KDA_ERR_SHAPE;
   if (d->n_seqs == 0) return KDA_OK;
   if (!d->state || !d->q || !d->k || !d->v || !d->beta || !d->o) return KDA_ERR_NULL;
   const bool bf = d->dtype == KDA_DTYPE_BF16;
   // the state is read and written as 16-byte vectors; the rest element-wise
   if (!aligned(d->state, 16)) return KDA_ERR_ALIGN;
+  if (d->state_indices && !aligned(d->state_indices, 4)) return KDA_ERR_ALIGN;
   const void* pe[] = {d->q, d->k, d->v, d->beta, d->o};
   for (const void* p : pe)
     if (!aligned(p, bf ? 2 : 4)) return KDA_ERR_ALIGN;
@@ -240,12 +265,14 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   const int st = check_gate(d->gate, d->g, true, d->n_seqs, d->n_heads, D, es, &a.gate, rgate);
   if (st != KDA_OK) return st;
   const Range ro = range_of(d->o, NH * D * es);
-  const Range ins[] = {range_of(d->state, NH * D * D * 4), range_of(d->q, NH * D * es),
+  const int64_t NS = (d->state_indices ? (int64_t)d->n_slots : (int64_t)d->n_seqs) * d->n_heads;
+  const Range ins[] = {range_of(d->state, NS * D * D * 4), range_of(d->q, NH * D * es),
                        range_of(d->k, NH * D * es),        range_of(d->v, NH * D * es),
-                       rgate[0], rgate[1], rgate[2],       range_of(d->beta, NH * es)};
+                       rgate[0], rgate[1], rgate[2],       range_of(d->beta, NH * es),
+                       range_of(d->state_indices, d->state_indices ? (int64_t)d->n_seqs * 4 : 0)};
   for (const Range& r : ins)
     if (overlap(ro, r)) return KDA_ERR_ALIAS;
-  for (int i = 1; i < 8; ++i)
+  for (int i = 1; i < 9; ++i)
     if (overlap(ins[0], ins[i])) return KDA_ERR_ALIAS;
   a.bf16 = bf;
   a.n_seqs = d->n_seqs;
@@ -259,6 +286,8 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   a.g = d->g;
   a.beta = d->beta;
   a.o = d->o;
+  a.slots = d->state_indices;
+  a.n_slots = d->state_indices ? d->n_slots : 0;
   return hip_status(kda::launch_decode(a, (hipStream_t)stream));
 }
 

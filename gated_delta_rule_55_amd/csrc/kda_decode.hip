@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
                                                      const float* __restrict__ a_log,
                                                      const float* __restrict__ dt_bias,
                                                      int n_heads, const TIO* __restrict__ beta,
-                                                     TIO* __restrict__ o, float scale) {
+                                                     TIO* __restrict__ o, float scale,
+                                                     const int* __restrict__ slots, int n_slots) {
   constexpr int NQ = D / 4;       // column quads per row
   constexpr int RG = 256 / NQ;    // row groups
   constexpr int RPT = D / RG;     // rows per thread
@@ -49,7 +50,15 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   const int cq = tid % NQ;
   const int rg = tid / NQ;
   const int64_t nh = blockIdx.x;
-  float* S = state + nh * (int64_t)(D * D);
+  // the state of sequence n lives in pool slot slots[n] (n without a slot
+  // table); a negative slot skips the sequence: nothing is read or written
+  int64_t sh = nh;
+  if (slots) {
+    const int slot = slots[nh / n_heads];
+    if (slot < 0 || slot >= n_slots) return;
+    sh = (int64_t)slot * n_heads + nh % n_heads;
+  }
+  float* S = state + sh * (int64_t)(D * D);
 
   // Issue every state load first: rows rg + RG * i, columns 4cq .. 4cq + 3.
   f32x4 s[RPT];
@@ -111,6 +120,158 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   }
 }
 
+// Recurrent prefill: the decode step run over each sequence's tokens in
+// order, the state held in registers from the first token to the last (one
+// read and one write of the state per sequence).  The pages run decode and
+// continuing prefills (T >= 1 new tokens on a carried state) through this
+// recurrent op (page "model(kimi_linear): ONE-SURFACE ROW 7 -- fold
+// Kimi-Linear onto the shared paged runner", B2: KdaGatedDeltaRule for decode
+// and continuing prefills over the state pool keyed by state indices).
+// One 256-thread workgroup per (sequence, head), tiled like decode_kernel;
+// token t + 1's inputs are loaded while token t computes.  cu_seqlens is read
+// clamped to [0, t_total], so any contents stay in bounds.
+template <typename TIO, int D, bool GATE>
+__global__ __launch_bounds__(256) void recurrent_kernel(
+    const float* __restrict__ h0, float* __restrict__ ht, const TIO* __restrict__ q,
+    const TIO* __restrict__ k, const TIO* __restrict__ v, const float* __restrict__ g,
+    const TIO* __restrict__ gx, const float* __restrict__ a_log,
+    const float* __restrict__ dt_bias, const TIO* __restrict__ beta, TIO* __restrict__ o,
+    float scale, int n_heads, int64_t t_total, const int* __restrict__ cu,
+    const int* __restrict__ slots, int n_slots) {
+  constexpr int NQ = D / 4;
+  constexpr int RG = 256 / NQ;
+  constexpr int RPT = D / RG;
+  static_assert(NQ * RG == 256 && RG * RPT == D, "recurrent tiling");
+
+  __shared__ float s_q[2][D], s_k[2][D], s_d[2][D], s_v[2][D], s_u[D];
+  __shared__ float s_red[2][RG][D];
+  __shared__ float s_kq, s_b[2];
+
+  const int tid = threadIdx.x;
+  const int cq = tid % NQ;
+  const int rg = tid / NQ;
+  const int n = blockIdx.x / n_heads, h = blockIdx.x % n_heads;
+  int slot = n;
+  if (slots) {
+    slot = slots[n];
+    if (slot < 0 || slot >= n_slots) return;
+  }
+  int64_t t0 = cu ? cu[n] : 0, t1 = cu ? cu[n + 1] : t_total;
+  t0 = t0 < 0 ? 0 : (t0 > t_total ? t_total : t0);
+  t1 = t1 < t0 ? t0 : (t1 > t_total ? t_total : t1);
+  const int64_t sb = ((int64_t)slot * n_heads + h) * (int64_t)(D * D);
+
+  f32x4 s[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    s[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + sb + (rg + RG * i) * D + 4 * cq) : zero4();
+
+  const float ea = GATE ? __expf(a_log[h]) : 1.f;
+  const float bias_c = (GATE && tid < D) ? dt_bias[h * D + tid] : 0.f;
+  // this thread's element of one token (tid < D), loaded ahead
+  TIO rq{}, rk{}, rv{}, rx{}, rb{};
+  float rg_{};
+  auto fetch = [&](int64_t t) {
+    if (tid < D) {
+      const int64_t at = (t * n_heads + h) * D + tid;
+      rq = q[at];
+      rk = k[at];
+      rv = v[at];
+      if constexpr (GATE) rx = gx[at];
+      else rg_ = g[at];
+    }
+    if (tid == 0) rb = beta[t * n_heads + h];
+  };
+  if (t0 < t1) fetch(t0);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int pb = (int)(t & 1);
+    if (tid < D) {
+      s_q[pb][tid] = to_f32(rq);
+      s_k[pb][tid] = to_f32(rk);
+      s_v[pb][tid] = to_f32(rv);
+      if constexpr (GATE) s_d[pb][tid] = fast_exp2(kimi_gate_log2(to_f32(rx) + bias_c, ea));
+      else s_d[pb][tid] = __expf(rg_);
+    }
+    if (tid == 0) s_b[pb] = to_f32(rb);
+    __syncthreads();
+    if (t + 1 < t1) fetch(t + 1);
+    if (tid < 64) {  // k . q by one wave
+      float acc = 0.f;
+      for (int i = tid; i < D; i += 64) acc += s_k[pb][i] * s_q[pb][i];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+      if (tid == 0) s_kq = acc;
+    }
+    f32x4 pk = zero4(), pq = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      s[i] *= s_d[pb][r];
+      pk += s[i] * s_k[pb][r];
+      pq += s[i] * s_q[pb][r];
+    }
+    *reinterpret_cast<f32x4*>(&s_red[0][rg][4 * cq]) = pk;
+    *reinterpret_cast<f32x4*>(&s_red[1][rg][4 * cq]) = pq;
+    __syncthreads();
+    if (tid < D) {
+      float p = 0.f, r = 0.f;
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        p += s_red[0][j][tid];
+        r += s_red[1][j][tid];
+      }
+      const float u = s_b[pb] * (s_v[pb][tid] - p);
+      s_u[tid] = u;
+      o[(t * n_heads + h) * D + tid] = from_f32<TIO>(scale * (r + s_kq * u));
+    }
+    __syncthreads();
+    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      s[i] += s_k[pb][r] * u4;
+    }
+  }
+  if (ht) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      *reinterpret_cast<f32x4*>(ht + sb + (rg + RG * i) * D + 4 * cq) = s[i];
+  }
+}
+
+template <typename TIO, int D>
+static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+  const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
+  if (a.gate.mode == GATE_KIMI_)
+    hipLaunchKernelGGL((recurrent_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
+                       a.g, (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias,
+                       (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
+                       a.cu_seqlens, a.slots, a.n_slots);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
+                       a.g, (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
+                       (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
+                       a.cu_seqlens, a.slots, a.n_slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
+  if ((int64_t)a.n_seqs * a.n_heads == 0) return hipSuccess;
+  const bool bf = a.bf16;
+  switch (a.d) {
+    case 32:
+      return bf ? launch_recurrent_t<bf16, 32>(a, stream) : launch_recurrent_t<float, 32>(a, stream);
+    case 64:
+      return bf ? launch_recurrent_t<bf16, 64>(a, stream) : launch_recurrent_t<float, 64>(a, stream);
+    case 128:
+      return bf ? launch_recurrent_t<bf16, 128>(a, stream)
+                : launch_recurrent_t<float, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename TIO, int D>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
@@ -118,12 +279,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0, stream,
                        a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias, a.n_heads,
-                       (const TIO*)a.beta, (TIO*)a.o, a.scale);
+                       (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots);
   else
     hipLaunchKernelGGL((decode_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0, stream,
                        a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
-                       a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale);
+                       a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots);
   return hipGetLastError();
 }
 

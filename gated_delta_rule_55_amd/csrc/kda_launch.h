@@ -30,6 +30,8 @@ struct DecodeArgs {
   const void* beta;
   void* o;
   GateArgs gate;
+  const int* slots = nullptr;  // state pool slot per sequence, or NULL (slot n)
+  int n_slots = 0;
 };
 
 // Launch plans (same values as kda_plan in include/kda.h).
@@ -50,7 +52,14 @@ struct PrefillArgs {
   void* o;
   float* ht;
   GateArgs gate;
+  const int* slots = nullptr;  // h0 / ht pool slot per sequence, or NULL (slot n)
+  int n_slots = 0;
 };
+
+// Recurrent (token-by-token) prefill: the prefill arguments without chunk,
+// plan or workspace.
+using RecurrentArgs = PrefillArgs;
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
 // Upper bound on the number of chunks: sum_n ceil(L_n / C) <= T / C + N.
 inline int64_t max_chunks(int64_t t_total, int n_seqs, int chunk) {

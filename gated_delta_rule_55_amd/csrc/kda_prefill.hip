@@ -199,7 +199,8 @@ template <typename TIO, int D, int C>
 __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     const float* __restrict__ h0, float* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
     int n_heads, const int* __restrict__ status, const int* __restrict__ chunk_off,
-    const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks) {
+    const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks,
+    const int* __restrict__ slots, int n_slots) {
   using Gm = Geo<TIO, D, C>;
   using SS = ScanStep<TIO, D, C>;
   constexpr int NB = D / 16;
@@ -217,9 +218,16 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
 
+  // h0 / ht of sequence n live in pool slot slots[n] (slot n without a slot
+  // table); a negative slot skips the sequence (no o, no state)
+  int slot = n;
+  if (slots) {
+    slot = slots[n];
+    if (slot < 0 || slot >= n_slots) return;
+  }
   SS::clear_vt(lds);
   f32x4 S[2];
-  const size_t sbase = ((size_t)n * n_heads + h) * D * D;
+  const size_t sbase = ((size_t)slot * n_heads + h) * D * D;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -621,7 +629,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
     const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * (D / 16));
     hipLaunchKernelGGL((state_scan_kernel<TIO, D, C>), dim3(nblk), dim3(64 * (D / 32)),
                        Gm::SCAN_LDS, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
-                       chunk_off, tab, blocks);
+                       chunk_off, tab, blocks, a.slots, a.n_slots);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
     return hipSuccess;

@@ -64,7 +64,8 @@ def _check_gate(gate, g, lead, H, dk, dtype, dev):
 
 
 def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
-                 ht=None, plan="auto", gate=None) -> _abi.PrefillDesc:
+                 ht=None, plan="auto", gate=None, state_indices=None,
+                 n_slots=0) -> _abi.PrefillDesc:
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
@@ -72,7 +73,47 @@ def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=6
         dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv, chunk=int(chunk),
         plan=_PLANS[plan], t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
         v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
-        o=_ptr(o), ht=_ptr(ht), gate=_gate_tuple(gate))
+        o=_ptr(o), ht=_ptr(ht), gate=_gate_tuple(gate), state_indices=_ptr(state_indices),
+        n_slots=int(n_slots))
+
+
+def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht, output_final_state, gate,
+                  state_indices, state_pool_slots):
+    """Shared checks of the prefill entry points; returns (N, n_slots, out, ht)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("the KDA prefill runs on the GPU only")
+    if q.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    _check(q, "q", (T, H, dk), q.dtype, dev)
+    _check(k, "k", (T, H, dk), q.dtype, dev)
+    _check(v, "v", (T, H, dv), q.dtype, dev)
+    _check_gate(gate, g, (T,), H, dk, q.dtype, dev)
+    _check(beta, "beta", (T, H), q.dtype, dev)
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    S = N
+    if state_indices is not None:
+        _check(state_indices, "state_indices", (N,), torch.int32, dev)
+        pool = h0 if h0 is not None else ht
+        if pool is None:
+            raise ValueError("state_indices needs a state pool (h0 and/or ht)")
+        S = int(pool.shape[0])
+    if h0 is not None:
+        _check(h0, "h0", (S, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    else:
+        _check(out, "out", (T, H, dv), q.dtype, dev)
+    if ht is None and output_final_state:
+        ht = h0 if state_indices is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
+                                                                device=dev)
+    if ht is not None:
+        _check(ht, "ht", (S, H, dk, dv), torch.float32, dev)
+    return N, (S if state_indices is not None else 0), out, ht
 
 
 def prefill_workspace_bytes(T: int, H: int, d: int, n_seqs: int = 1, chunk: int = 64,
@@ -88,7 +129,9 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   chunk: int = 64, out: Optional[torch.Tensor] = None,
                   ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   output_final_state: bool = True, stream=None, events=None,
-                  plan: str = "auto", gate=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  plan: str = "auto", gate=None,
+                  state_indices: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
     h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
     None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
@@ -99,33 +142,14 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     chunk-local stage).  `plan`: "auto", "fused" or "two_pass".  `gate`: None
     (g given), or (x [T, H, dk] in q's dtype, a_log [H] fp32, dt_bias [H, dk]
     fp32) to compute g = -exp(a_log) softplus(x + dt_bias) in the kernels
-    (g may then be None)."""
+    (g may then be None).  `state_indices` (int32 [N] on the device): h0 and
+    ht are then state pools [S, H, dk, dv] (ht defaults to h0: in place) and
+    sequence n uses slot state_indices[n]; a negative slot skips it."""
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("chunk_prefill runs on the GPU only")
-    if q.dtype not in _DTYPES:
-        raise TypeError(f"unsupported dtype {q.dtype}")
-    T, H, dk = q.shape
-    dv = v.shape[-1]
-    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
-    _check(k, "k", (T, H, dk), q.dtype, dev)
-    _check(v, "v", (T, H, dv), q.dtype, dev)
-    _check_gate(gate, g, (T,), H, dk, q.dtype, dev)
-    _check(beta, "beta", (T, H), q.dtype, dev)
-    _check(q, "q", (T, H, dk), q.dtype, dev)
-    if h0 is not None:
-        _check(h0, "h0", (N, H, dk, dv), torch.float32, dev)
-    if cu_seqlens is not None:
-        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
-    if out is None:
-        out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
-    else:
-        _check(out, "out", (T, H, dv), q.dtype, dev)
-    if ht is None and output_final_state:
-        ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif ht is not None:
-        _check(ht, "ht", (N, H, dk, dv), torch.float32, dev)
-    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate)
+    N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
+                                        output_final_state, gate, state_indices, None)
+    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate,
+                        state_indices, n_slots)
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -138,19 +162,47 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     return out, ht
 
 
+def recurrent_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      g: Optional[torch.Tensor], beta: torch.Tensor,
+                      h0: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, ht: Optional[torch.Tensor] = None,
+                      output_final_state: bool = True, stream=None, gate=None,
+                      state_indices: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The prefill of chunk_prefill computed token by token with the state held
+    on chip (for continuing prefills of a few tokens on a carried state).  Same
+    arguments and results; no chunk, plan or workspace."""
+    N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
+                                        output_final_state, gate, state_indices, None)
+    desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, 64, out, ht, "auto", gate,
+                        state_indices, n_slots)
+    st = _abi.recurrent_prefill_raw(desc, _stream(stream))
+    if st != _abi.KDA_OK:
+        raise _abi.KdaError(st, "kda_recurrent_prefill")
+    return out, ht
+
+
 def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      g: Optional[torch.Tensor], beta: torch.Tensor, scale: Optional[float] = None,
-                     out: Optional[torch.Tensor] = None, stream=None, gate=None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, stream=None, gate=None,
+                     state_indices: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One recurrent decode step; `state` [N, H, dk, dv] fp32 is updated in place.
     q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].  Returns o [N, H, dv].
-    `gate` as in chunk_prefill (x is [N, H, dk])."""
+    `gate` as in chunk_prefill (x is [N, H, dk]).  `state_indices` (int32 [N]
+    on the device): `state` is then a pool [S, H, dk, dv] and sequence n
+    updates slot state_indices[n]; a negative slot skips it (its o is left as
+    it was)."""
     dev = state.device
     if dev.type != "cuda":
         raise ValueError("recurrent_decode runs on the GPU only")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    N, H, dk, dv = state.shape
-    _check(state, "state", (N, H, dk, dv), torch.float32, dev)
+    S, H, dk, dv = state.shape
+    N = S if state_indices is None else int(q.shape[0])
+    _check(state, "state", (S, H, dk, dv), torch.float32, dev)
+    if state_indices is not None:
+        _check(state_indices, "state_indices", (N,), torch.int32, dev)
     _check(q, "q", (N, H, dk), q.dtype, dev)
     _check(k, "k", (N, H, dk), q.dtype, dev)
     _check(v, "v", (N, H, dv), q.dtype, dev)
@@ -163,7 +215,9 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     desc = _abi.decode_desc(dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv,
                             scale=0.0 if scale is None else float(scale), state=state.data_ptr(),
                             q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=_ptr(g),
-                            beta=beta.data_ptr(), o=out.data_ptr(), gate=_gate_tuple(gate))
+                            beta=beta.data_ptr(), o=out.data_ptr(), gate=_gate_tuple(gate),
+                            state_indices=_ptr(state_indices),
+                            n_slots=S if state_indices is not None else 0)
     st = _abi.recurrent_decode_raw(desc, _stream(stream))
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_recurrent_decode")

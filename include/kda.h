@@ -141,6 +141,13 @@ typedef struct {
   float* ht;                  /* NULL = final state not returned               */
   kda_gate_desc gate;         /* g, or the raw gate and its parameters; g may  */
                               /* be NULL when gate.mode = KIMI                 */
+  const int32_t* state_indices; /* NULL, or device [N]: h0 and ht are state    */
+                              /* pools [n_slots, H, dk, dv] and sequence n     */
+                              /* reads h0[state_indices[n]], writes ht[..] ;   */
+                              /* a negative index (or one >= n_slots) skips    */
+                              /* the sequence: no o, no state.  Indices must   */
+                              /* be distinct.                                  */
+  int32_t n_slots;            /* pool size when state_indices is set           */
 } kda_prefill_desc;
 
 /* One recurrent decode step for a batch of N sequences, one token each.
@@ -161,7 +168,24 @@ typedef struct {
   const void* beta;
   void* o;
   kda_gate_desc gate;         /* as in kda_prefill_desc; x is [N, H, dk]        */
+  const int32_t* state_indices; /* NULL, or device [N]: state is a pool        */
+                              /* [n_slots, H, dk, dv], sequence n updates slot */
+                              /* state_indices[n]; negative (or >= n_slots)    */
+                              /* skips it (no o).  Indices must be distinct.   */
+  int32_t n_slots;            /* pool size when state_indices is set           */
 } kda_decode_desc;
+
+/* Recurrent prefill: the same computation as kda_chunk_prefill (same
+ * descriptor; chunk and plan are ignored, no workspace), run token by token
+ * with each (sequence, head) state held on chip from the first token to the
+ * last.  For continuing prefills of a few tokens on a carried state, where
+ * the chunked form has nothing to amortise (page "model(kimi_linear):
+ * ONE-SURFACE ROW 7 -- fold Kimi-Linear onto the shared paged runner", B2:
+ * the recurrent op serves decode and continuing prefills).  cu_seqlens is
+ * read clamped to [0, t_total]: contents that break the rules give
+ * unspecified o and ht but no access out of bounds.  fp32 and bf16 at every
+ * supported head dim. */
+int kda_recurrent_prefill(const kda_prefill_desc* d, void* stream);
 
 /* KDA_ABI_VERSION of the loaded library. */
 int kda_abi_version(void);

@@ -150,6 +150,29 @@ def test_decode_gate_validation(abi):
 
 
 @no_gpu_only
+def test_state_pool_and_recurrent_validation(abi):
+    # a slot table needs a pool size; indices are 4-byte aligned
+    d = _valid_prefill(abi, state_indices=0xb00000, n_slots=0)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == abi.KDA_ERR_SHAPE
+    d = _valid_prefill(abi, state_indices=0xb00002, n_slots=4)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == abi.KDA_ERR_ALIGN
+    # the recurrent prefill ignores chunk and plan but checks everything else
+    d = _valid_prefill(abi, chunk=48, plan=abi.KDA_PLAN_FUSED, q=0x100008)
+    assert abi.chunk_prefill_raw(d, 0x10000000, 1 << 30, 0) == abi.KDA_ERR_UNSUPPORTED
+    assert abi.recurrent_prefill_raw(d, 0) == abi.KDA_ERR_ALIGN
+    d = _valid_prefill(abi, o=0x100000 + 64)
+    assert abi.recurrent_prefill_raw(d, 0) == abi.KDA_ERR_ALIAS
+    kw = dict(dtype=abi.KDA_DTYPE_BF16, n_seqs=2, n_heads=2, dk=64, dv=64, state=0x100000,
+              q=0x900000, k=0xa00000, v=0xb00000, g=0xc00000, beta=0xd00000, o=0xe00000)
+    assert abi.recurrent_decode_raw(abi.decode_desc(**kw, state_indices=0xf00000, n_slots=0),
+                                    0) == abi.KDA_ERR_SHAPE
+    # with a pool of 40 slots the state spans 40 x 2 x 64 x 64 x 4 bytes: o inside it
+    assert abi.recurrent_decode_raw(abi.decode_desc(**dict(kw, o=0x100000 + 2 * 2 * 64 * 64 * 4 + 64),
+                                                    state_indices=0xf00000, n_slots=40),
+                                    0) == abi.KDA_ERR_ALIAS
+
+
+@no_gpu_only
 def test_fused_plan_is_switched_off(abi):
     """A fused-plan request is refused on the host, before any launch."""
     d = _valid_prefill(abi, plan=abi.KDA_PLAN_FUSED)
