@@ -1,4 +1,4 @@
-"""ctypes mirror of include/kda.h.  Loads the in-tree libkda.so; there is no
+"""ctypes mirror of include/kda.h and include/kda_conv.h.  Loads the in-tree libkda.so; there is no
 other implementation to fall back to, so a missing library is an error."""
 from __future__ import annotations
 
@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
-KDA_ABI_VERSION = 2
+KDA_ABI_VERSION = 3
 KDA_OK = 0
 KDA_ERR_NULL = -1
 KDA_ERR_SHAPE = -2
@@ -31,6 +31,9 @@ KDA_DTYPE_BF16 = 2
 
 KDA_GATE_GIVEN = 0
 KDA_GATE_KIMI = 1
+
+KDA_CONV_ACT_NONE = 0
+KDA_CONV_ACT_SILU = 1
 
 
 class GateDesc(ctypes.Structure):
@@ -91,6 +94,29 @@ class DecodeDesc(ctypes.Structure):
     ]
 
 
+class ConvDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("dtype", ctypes.c_int32),
+        ("n_seqs", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("width", ctypes.c_int32),
+        ("activation", ctypes.c_int32),
+        ("t_total", ctypes.c_int64),
+        ("x", ctypes.c_void_p),
+        ("weight", ctypes.c_void_p),
+        ("bias", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("state_in", ctypes.c_void_p),
+        ("state_out", ctypes.c_void_p),
+        ("state_indices", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int32),
+        ("n_out", ctypes.c_int32),
+        ("y", ctypes.c_void_p * 3),
+        ("y_width", ctypes.c_int32 * 3),
+    ]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -132,6 +158,10 @@ def lib():
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_prefill.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p]
         L.kda_recurrent_prefill.restype = ctypes.c_int
+        for name in ("kda_causal_conv1d_fwd", "kda_causal_conv1d_update"):
+            fn = getattr(L, name)
+            fn.argtypes = [ctypes.POINTER(ConvDesc), ctypes.c_void_p]
+            fn.restype = ctypes.c_int
         if L.kda_abi_version() != KDA_ABI_VERSION:
             raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != {KDA_ABI_VERSION}")
         _LIB = L
@@ -162,6 +192,18 @@ def decode_desc(**kw) -> DecodeDesc:
     d = DecodeDesc()
     d.struct_size = ctypes.sizeof(DecodeDesc)
     return _fill(d, kw)
+
+
+def conv_desc(**kw) -> ConvDesc:
+    d = ConvDesc()
+    d.struct_size = ctypes.sizeof(ConvDesc)
+    for key, val in kw.items():
+        if key in ("y", "y_width"):
+            for i, v in enumerate(val):
+                getattr(d, key)[i] = v
+        else:
+            setattr(d, key, val)
+    return d
 
 
 def workspace_bytes(desc: PrefillDesc) -> int:
@@ -196,3 +238,11 @@ def recurrent_prefill_raw(desc: PrefillDesc, stream: int) -> int:
 
 def workspace_status(workspace: int, stream: int) -> int:
     return int(lib().kda_workspace_status(workspace, stream))
+
+
+def conv_fwd_raw(desc: ConvDesc, stream: int) -> int:
+    return int(lib().kda_causal_conv1d_fwd(ctypes.byref(desc), stream))
+
+
+def conv_update_raw(desc: ConvDesc, stream: int) -> int:
+    return int(lib().kda_causal_conv1d_update(ctypes.byref(desc), stream))

@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "kda.h"
+#include "kda_conv.h"
 #include "kda_launch.h"
 
 namespace {
@@ -157,6 +158,90 @@ int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range
   return KDA_OK;
 }
 
+// The conv descriptor, for the forward (fwd = true) or the one-token update.
+int check_conv(const kda_conv_desc* d, bool fwd, kda::ConvArgs* a) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->struct_size != sizeof(kda_conv_desc)) return KDA_ERR_VERSION;
+  if (d->dtype != KDA_DTYPE_F32 && d->dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE;
+  const int W = d->width ? d->width : 4;
+  if (W < 2 || W > 4) return KDA_ERR_UNSUPPORTED;
+  if (d->activation != KDA_CONV_ACT_NONE && d->activation != KDA_CONV_ACT_SILU)
+    return KDA_ERR_UNSUPPORTED;
+  if (d->n_seqs < (fwd ? 1 : 0) || d->dim < 8 || d->dim % 8) return KDA_ERR_SHAPE;
+  const int64_t rows = fwd ? d->t_total : d->n_seqs;
+  if (rows < 0 || rows > INT32_MAX) return KDA_ERR_SHAPE;
+  if (d->state_indices && d->n_slots < 1) return KDA_ERR_SHAPE;
+  const int n_out = d->n_out ? d->n_out : 1;
+  if (n_out < 1 || n_out > 3) return KDA_ERR_SHAPE;
+  a->y_off[0] = 0;
+  for (int i = 0; i < n_out; ++i) {
+    int w = d->y_width[i];
+    if (n_out == 1 && w == 0) w = d->dim;
+    if (w < 8 || w % 8 || (int64_t)a->y_off[i] + w > d->dim) return KDA_ERR_SHAPE;
+    a->y_off[i + 1] = a->y_off[i] + w;
+  }
+  if (a->y_off[n_out] != d->dim) return KDA_ERR_SHAPE;
+  for (int i = n_out + 1; i < 4; ++i) a->y_off[i] = d->dim;
+  // workgroups the launches need (one per 16-byte channel vector group)
+  const int64_t vn = d->dtype == KDA_DTYPE_BF16 ? 8 : 4;
+  const int64_t ncb = (d->dim / vn + 255) / 256;
+  if ((rows + 15) / 16 * ncb + (int64_t)d->n_seqs * ncb > INT32_MAX) return KDA_ERR_SHAPE;
+
+  const bool work = rows > 0;
+  if (!d->weight || (work && !d->x)) return KDA_ERR_NULL;
+  if (fwd && !d->cu_seqlens && d->n_seqs != 1) return KDA_ERR_NULL;
+  for (int i = 0; i < n_out; ++i)
+    if (work && !d->y[i]) return KDA_ERR_NULL;
+  const void* p16[] = {d->x, d->weight, d->bias, d->state_in, d->state_out, d->y[0],
+                       n_out > 1 ? d->y[1] : nullptr, n_out > 2 ? d->y[2] : nullptr};
+  for (const void* p : p16)
+    if (p && !aligned(p, 16)) return KDA_ERR_ALIGN;
+  if ((d->state_indices && !aligned(d->state_indices, 4)) ||
+      (fwd && d->cu_seqlens && !aligned(d->cu_seqlens, 4)))
+    return KDA_ERR_ALIGN;
+
+  const int64_t es = vn == 8 ? 2 : 4, dim = d->dim, N = d->n_seqs;
+  const int64_t n_state = d->state_indices ? d->n_slots : N;
+  const Range rst_in = range_of(d->state_in, d->state_in ? n_state * (W - 1) * dim * es : 0),
+              rst_out = range_of(d->state_out, d->state_out ? n_state * (W - 1) * dim * es : 0);
+  const Range ins[] = {range_of(d->x, rows * dim * es), range_of(d->weight, dim * W * 4),
+                       range_of(d->bias, d->bias ? dim * 4 : 0), rst_in,
+                       range_of(fwd ? d->cu_seqlens : nullptr, fwd && d->cu_seqlens ? (N + 1) * 4 : 0),
+                       range_of(d->state_indices, d->state_indices ? N * 4 : 0)};
+  Range ry[3];
+  for (int i = 0; i < n_out; ++i) {
+    ry[i] = range_of(d->y[i], rows * (a->y_off[i + 1] - a->y_off[i]) * es);
+    for (const Range& r : ins)
+      if (overlap(ry[i], r)) return KDA_ERR_ALIAS;
+    if (overlap(ry[i], rst_out)) return KDA_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlap(ry[i], ry[j])) return KDA_ERR_ALIAS;
+  }
+  // state_out may be exactly state_in, never partly over it or another input
+  if (d->state_out && d->state_in && d->state_out != d->state_in && overlap(rst_out, rst_in))
+    return KDA_ERR_ALIAS;
+  for (const Range& r : ins)
+    if (&r != &ins[3] && overlap(rst_out, r)) return KDA_ERR_ALIAS;
+
+  a->bf16 = d->dtype == KDA_DTYPE_BF16;
+  a->n_seqs = d->n_seqs;
+  a->dim = d->dim;
+  a->width = W;
+  a->act = d->activation;
+  a->rows = rows;
+  a->x = d->x;
+  a->weight = d->weight;
+  a->bias = d->bias;
+  a->cu_seqlens = fwd ? d->cu_seqlens : nullptr;
+  a->state_in = d->state_in;
+  a->state_out = d->state_out;
+  a->slots = d->state_indices;
+  a->n_slots = d->state_indices ? d->n_slots : 0;
+  a->n_out = n_out;
+  for (int i = 0; i < 3; ++i) a->y[i] = i < n_out ? d->y[i] : nullptr;
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +374,20 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   a.slots = d->state_indices;
   a.n_slots = d->state_indices ? d->n_slots : 0;
   return hip_status(kda::launch_decode(a, (hipStream_t)stream));
+}
+
+int kda_causal_conv1d_fwd(const kda_conv_desc* d, void* stream) {
+  kda::ConvArgs a;
+  const int st = check_conv(d, true, &a);
+  if (st != KDA_OK) return st;
+  return hip_status(kda::launch_conv_fwd(a, (hipStream_t)stream));
+}
+
+int kda_causal_conv1d_update(const kda_conv_desc* d, void* stream) {
+  kda::ConvArgs a;
+  const int st = check_conv(d, false, &a);
+  if (st != KDA_OK) return st;
+  return hip_status(kda::launch_conv_update(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -75,6 +75,31 @@ hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t str
                           const hipEvent_t* events);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Short causal conv (values of kda_conv_act in include/kda_conv.h).
+constexpr int CONV_NONE_ = 0;
+constexpr int CONV_SILU_ = 1;
+
+struct ConvArgs {
+  bool bf16;
+  int n_seqs, dim, width, act;
+  int64_t rows;                 // t_total (forward) or n_seqs (update)
+  const void* x;
+  const float* weight;
+  const float* bias;            // may be NULL
+  const int32_t* cu_seqlens;    // forward; may be NULL when n_seqs == 1
+  const void* state_in;         // may be NULL (zero taps)
+  void* state_out;              // may be NULL, or equal to state_in
+  const int* slots = nullptr;   // state slot per sequence, or NULL (slot n)
+  int n_slots = 0;
+  int n_out;                    // output column blocks, 1..3
+  void* y[3];
+  int y_off[4];                 // first channel of each block; y_off[n_out] = dim
+};
+// Workgroups the forward launches (both kernels).
+int64_t conv_fwd_blocks(const ConvArgs& a);
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t stream);
+hipError_t launch_conv_update(const ConvArgs& a, hipStream_t stream);
+
 // Offset of the device status word inside a prefill workspace.
 constexpr size_t kWsStatusOffset = 0;
 

@@ -227,3 +227,98 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
 def workspace_status(workspace: torch.Tensor, stream=None) -> int:
     """Device status word of the last prefill that used `workspace`."""
     return _abi.workspace_status(workspace.data_ptr(), _stream(stream))
+
+
+_ACTS = {None: _abi.KDA_CONV_ACT_NONE, "none": _abi.KDA_CONV_ACT_NONE,
+         "silu": _abi.KDA_CONV_ACT_SILU}
+
+
+def _conv_args(x, weight, bias, state_in, state_out, state_indices, n_seqs, split, out,
+               activation):
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("the causal conv runs on the GPU only")
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if activation not in _ACTS:
+        raise ValueError(f"activation must be one of {list(_ACTS)}")
+    rows, dim = x.shape
+    _check(x, "x", (rows, dim), x.dtype, dev)
+    if weight.dim() != 2 or weight.shape[0] != dim:
+        raise ValueError(f"weight must be [dim={dim}, W], got {tuple(weight.shape)}")
+    W = int(weight.shape[1])
+    _check(weight, "weight", (dim, W), torch.float32, dev)
+    if bias is not None:
+        _check(bias, "bias", (dim,), torch.float32, dev)
+    S = n_seqs if state_indices is None else None
+    for name, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None:
+            if S is None:
+                S = int(st.shape[0])
+            _check(st, name, (S, W - 1, dim), x.dtype, dev)
+    if state_indices is not None:
+        _check(state_indices, "state_indices", (n_seqs,), torch.int32, dev)
+        if S is None:
+            S = 1  # no state buffer: the slots only select which sequences run
+    widths = (dim,) if split is None else tuple(int(w) for w in split)
+    if sum(widths) != dim or not 1 <= len(widths) <= 3:
+        raise ValueError(f"split {widths} must be 1..3 widths summing to dim={dim}")
+    if out is None:
+        ys = tuple(torch.empty((rows, w), dtype=x.dtype, device=dev) for w in widths)
+    else:
+        ys = (out,) if isinstance(out, torch.Tensor) else tuple(out)
+        if len(ys) != len(widths):
+            raise ValueError("out must match split")
+        for i, (y, w) in enumerate(zip(ys, widths)):
+            _check(y, f"out[{i}]", (rows, w), x.dtype, dev)
+    desc = _abi.conv_desc(dtype=_DTYPES[x.dtype], n_seqs=n_seqs, dim=dim, width=W,
+                          activation=_ACTS[activation], x=x.data_ptr(),
+                          weight=weight.data_ptr(), bias=_ptr(bias), state_in=_ptr(state_in),
+                          state_out=_ptr(state_out), state_indices=_ptr(state_indices),
+                          n_slots=S if state_indices is not None else 0, n_out=len(widths),
+                          y=[y.data_ptr() for y in ys] + [None] * (3 - len(ys)),
+                          y_width=list(widths) + [0] * (3 - len(widths)))
+    return desc, (ys[0] if split is None else ys)
+
+
+def causal_conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None,
+                      state_in: Optional[torch.Tensor] = None,
+                      state_out: Optional[torch.Tensor] = None,
+                      state_indices: Optional[torch.Tensor] = None, activation="silu",
+                      split=None, out=None, stream=None):
+    """Short causal depthwise conv over a packed batch with carried taps.
+
+    x [T, dim] (fp32 or bf16); weight [dim, W] fp32, W in 2..4; bias [dim]
+    fp32; cu_seqlens int32 [N + 1] (None for one sequence); state_in /
+    state_out [S, W - 1, dim] in x.dtype (None: zero taps in / none out; may be
+    the same tensor), S = N or the pool size with state_indices (int32 [N],
+    negative = skip the sequence).  split: None returns y [T, dim]; a tuple of
+    1..3 widths returns that many dense [T, w] tensors (e.g. q, k, v)."""
+    N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
+    if cu_seqlens is not None:
+        _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, x.device)
+    desc, y = _conv_args(x, weight, bias, state_in, state_out, state_indices, N, split, out,
+                         activation)
+    desc.t_total = int(x.shape[0])
+    desc.cu_seqlens = _ptr(cu_seqlens)
+    st = _abi.conv_fwd_raw(desc, _stream(stream))
+    if st != _abi.KDA_OK:
+        raise _abi.KdaError(st, "kda_causal_conv1d_fwd")
+    return y
+
+
+def causal_conv1d_update(x: torch.Tensor, weight: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None,
+                         state: Optional[torch.Tensor] = None,
+                         state_indices: Optional[torch.Tensor] = None, activation="silu",
+                         split=None, out=None, stream=None):
+    """One token per sequence: x [N, dim]; `state` [S, W - 1, dim] is read and
+    shifted in place (S = N, or the pool size with state_indices).  Returns y
+    as causal_conv1d_fwd does."""
+    desc, y = _conv_args(x, weight, bias, state, state, state_indices, int(x.shape[0]), split,
+                         out, activation)
+    st = _abi.conv_update_raw(desc, _stream(stream))
+    if st != _abi.KDA_OK:
+        raise _abi.KdaError(st, "kda_causal_conv1d_update")
+    return y

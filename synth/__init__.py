@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for KDA prefill and decode.
+"""Seeded synthetic inputs for KDA prefill and decode and the short conv.
 
 This package only draws random numbers and rounds them to storage dtypes.  It
 holds none of the attention arithmetic, so the CPU oracle and the HIP path can
@@ -13,3 +13,4 @@ from .kda_inputs import (  # noqa: F401
     make_inputs,
     slice_heads,
 )
+from .conv_inputs import ConvInputs, make_conv_inputs, seeded_conv_lengths  # noqa: F401

@@ -36,9 +36,9 @@ def abi():
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("kda.h", "kda_conv.h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kda_[a-z_]+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kda_[a-z0-9_]+)\s*\(",
                        text, flags=re.M)
     return sorted(set(names))
 
@@ -46,6 +46,7 @@ def declared_functions():
 def test_exports_every_declared_symbol(abi):
     names = declared_functions()
     assert "kda_chunk_prefill" in names and "kda_recurrent_decode" in names
+    assert "kda_causal_conv1d_fwd" in names and "kda_causal_conv1d_update" in names
     lib = ctypes.CDLL(abi.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
@@ -61,13 +62,14 @@ def test_version_and_strings(abi):
 
 def test_struct_sizes_match_header(abi, tmp_path):
     src = tmp_path / "sz.c"
-    src.write_text('#include <stdio.h>\n#include "kda.h"\n'
-                   'int main(void){printf("%zu %zu", sizeof(kda_prefill_desc),'
-                   ' sizeof(kda_decode_desc));return 0;}\n')
+    src.write_text('#include <stdio.h>\n#include "kda_conv.h"\n'
+                   'int main(void){printf("%zu %zu %zu", sizeof(kda_prefill_desc),'
+                   ' sizeof(kda_decode_desc), sizeof(kda_conv_desc));return 0;}\n')
     exe = tmp_path / "sz"
     os.system(f"gcc -I{ROOT}/include {src} -o {exe}")
     out = os.popen(str(exe)).read().split()
-    assert [int(x) for x in out] == [ctypes.sizeof(abi.PrefillDesc), ctypes.sizeof(abi.DecodeDesc)]
+    assert [int(x) for x in out] == [ctypes.sizeof(abi.PrefillDesc), ctypes.sizeof(abi.DecodeDesc),
+                                     ctypes.sizeof(abi.ConvDesc)]
 
 
 def _valid_prefill(abi, **over):
@@ -220,6 +222,49 @@ def test_null_descriptors(abi):
 def test_decode_zero_batch_is_noop(abi):
     d = abi.decode_desc(dtype=abi.KDA_DTYPE_F32, n_seqs=0, n_heads=1, dk=32, dv=32)
     assert abi.recurrent_decode_raw(d, 0) == abi.KDA_OK
+
+
+def _valid_conv(abi, **over):
+    kw = dict(dtype=abi.KDA_DTYPE_BF16, n_seqs=2, dim=256, width=4, activation=1, t_total=100,
+              x=0x100000, weight=0x200000, bias=0x300000, cu_seqlens=0x400000,
+              state_in=0x500000, state_out=0x500000, n_out=1, y=[0x600000, None, None],
+              y_width=[256, 0, 0])
+    kw.update(over)
+    return abi.conv_desc(**kw)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("over,status", [
+    (dict(struct_size=4), -8), (dict(dtype=0), -3), (dict(width=5), -4), (dict(width=1), -4),
+    (dict(activation=2), -4), (dict(dim=260, y_width=[260, 0, 0]), -2), (dict(n_seqs=0), -2),
+    (dict(t_total=-1), -2), (dict(n_out=4), -2), (dict(n_out=2, y_width=[128, 64, 0]), -2),
+    (dict(n_out=2, y_width=[128, 132, 0], y=[0x600000, 0x700000, None]), -2),
+    (dict(weight=None), -1), (dict(x=None), -1), (dict(cu_seqlens=None), -1),
+    (dict(n_out=2, y_width=[128, 128, 0]), -1),                         # y[1] missing
+    (dict(x=0x100008), -5), (dict(bias=0x300004), -5), (dict(state_out=0x500008), -5),
+    (dict(y=[0x100000 + 4096, None, None]), -9),                        # y overlaps x
+    (dict(state_out=0x500000 + 512), -9),                               # partly over state_in
+    (dict(state_out=0x100000 + 1024, state_in=None), -9),               # state_out over x
+    (dict(state_indices=0x800000, n_slots=0), -2),
+])
+def test_conv_fwd_validation(abi, over, status):
+    d = _valid_conv(abi, **over)
+    if "struct_size" in over:
+        d.struct_size = over["struct_size"]
+    assert abi.conv_fwd_raw(d, 0) == status
+
+
+@no_gpu_only
+def test_conv_update_validation(abi):
+    d = _valid_conv(abi, n_seqs=0, x=None, y=[None, None, None])
+    assert abi.conv_update_raw(d, 0) == abi.KDA_OK              # nothing to do
+    d = _valid_conv(abi, cu_seqlens=None, x=0x100000 + 8)
+    assert abi.conv_update_raw(d, 0) == abi.KDA_ERR_ALIGN
+    d = _valid_conv(abi, cu_seqlens=None, y=[0x500000, None, None])
+    assert abi.conv_update_raw(d, 0) == abi.KDA_ERR_ALIAS       # y over the state
+    L = abi.lib()
+    assert L.kda_causal_conv1d_fwd(None, None) == abi.KDA_ERR_NULL
+    assert L.kda_causal_conv1d_update(None, None) == abi.KDA_ERR_NULL
 
 
 def test_product_path_fails_loudly_without_library(monkeypatch):
