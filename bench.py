@@ -48,6 +48,7 @@ DECODE_FLOPS = 64 * 32 * (7 * 128 * 128)
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["gated_delta_rule_55_amd/csrc/kda_prefill.hip",
+                  "gated_delta_rule_55_amd/csrc/kda_conv.hip",
                   "gated_delta_rule_55_amd/csrc/kda_chunk_ops.h",
                   "gated_delta_rule_55_amd/csrc/kda_decode.hip",
                   "gated_delta_rule_55_amd/csrc/kda_device.h"]
@@ -221,6 +222,87 @@ def bench_recurrent(args, torch, kda, inp, state0, dec, stream, R=16):
                                   f"{rbytes} bytes per call"}}
 
 
+CONV_DIM = 3 * 32 * 128  # [q|k|v] channels at H = 32, d = 128
+CONV_W = 4
+
+
+def bench_conv(args, torch, kda, T=32768, N_dec=64, reps=10, dec_calls=256):
+    """The short causal conv over the [q|k|v] channels (dim 12288, W = 4, SiLU,
+    bf16) that feeds the prefill: the varlen forward over the prefill-32k
+    tokens writing q, k, v as separate tensors and the new taps, then the
+    one-token update at the decode shape (64 sequences, 64-slot tap pool).
+    Inputs: N(0, 1) activations and taps, U(-1/2, 1/2) weight and bias, drawn
+    with a seeded device generator."""
+    dim, W = CONV_DIM, CONV_W
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(17)
+    x = torch.randn((T, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    w = torch.rand((dim, W), generator=gen, device="cuda") - 0.5
+    b = torch.rand((dim,), generator=gen, device="cuda") - 0.5
+    st0 = torch.randn((1, W - 1, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    st = st0.clone()
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    outs = tuple(torch.empty((T, dim // 3), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        kda.causal_conv1d_fwd(x, w, b, cu, st0, st, split=(dim // 3,) * 3, out=outs)
+
+    for _ in range(3):
+        fwd()
+    # back-to-back calls between the events keep the GPU busy, so the host's
+    # enqueue time of a call is not counted
+    times = []
+    for _ in range(reps):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            fwd()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e) / 10)
+    ms = statistics.median(times)
+    fbytes = 2 * T * dim * 2 + 2 * (W - 1) * dim * 2 + dim * (W + 1) * 4
+    fach = fbytes / (ms / 1e3) / 1e9
+    res = {"workload": f"causal conv forward over the prefill-32k tokens: T={T}, dim={dim} "
+                       f"([q|k|v], H=32, d=128), W={W}, SiLU, bf16, q/k/v written as separate "
+                       "tensors, carried taps in and out",
+           "ms_per_call": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(fach, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(fach / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("conv"),
+                        "scope": f"x read once, y written once, taps, weight and bias: "
+                                 f"{fbytes} bytes per call (both launches)"}}
+    del x, outs
+    # decode shape: one token for each of 64 sequences per call
+    xd = torch.randn((dec_calls, N_dec, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    pool = torch.randn((N_dec, W - 1, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    slots = torch.arange(N_dec, dtype=torch.int32, device="cuda")
+    yd = tuple(torch.empty((N_dec, dim // 3), dtype=torch.bfloat16, device="cuda")
+               for _ in range(3))
+    for i in range(3):
+        kda.causal_conv1d_update(xd[i], w, b, pool, state_indices=slots, split=(dim // 3,) * 3,
+                                 out=yd)
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(dec_calls):
+        kda.causal_conv1d_update(xd[i], w, b, pool, state_indices=slots, split=(dim // 3,) * 3,
+                                 out=yd)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ums = a.elapsed_time(e) / dec_calls
+    ubytes = 2 * N_dec * dim * 2 + 2 * N_dec * (W - 1) * dim * 2 + dim * (W + 1) * 4
+    uach = ubytes / (ums / 1e3) / 1e9
+    res["update"] = {
+        "workload": f"causal conv one-token update: {N_dec} sequences, dim={dim}, W={W}, SiLU, "
+                    f"bf16, {N_dec}-slot tap pool; {dec_calls} back-to-back calls",
+        "us_per_call": round(ums * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(uach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(uach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "scope": f"{ubytes} bytes per call; launch-bound at this size"}}
+    return res
+
+
 def cpu_prefill_baseline(args, inp):
     """The fp64 oracle (C, OpenMP over the 32 head chains) on the prefill-32k
     inputs: the whole sequence, repeated until about --cpu-seconds of CPU time
@@ -267,6 +349,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
     ap.add_argument("--no-gate", action="store_true", help="skip the fused-gate prefill leg")
+    ap.add_argument("--no-conv", action="store_true", help="skip the causal conv leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--plan", choices=["auto", "fused", "two_pass"], default="auto",
                     help="prefill launch plan")
@@ -353,6 +436,9 @@ def main():
             log("timing the CPU oracle (decode)")
             line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)
         del dec
+    if not args.no_conv:
+        log("causal conv leg")
+        line["causal_conv"] = bench_conv(args, torch, kda)
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")

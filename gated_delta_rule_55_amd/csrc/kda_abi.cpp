@@ -167,7 +167,9 @@ int check_conv(const kda_conv_desc* d, bool fwd, kda::ConvArgs* a) {
   if (W < 2 || W > 4) return KDA_ERR_UNSUPPORTED;
   if (d->activation != KDA_CONV_ACT_NONE && d->activation != KDA_CONV_ACT_SILU)
     return KDA_ERR_UNSUPPORTED;
-  if (d->n_seqs < (fwd ? 1 : 0) || d->dim < 8 || d->dim % 8) return KDA_ERR_SHAPE;
+  // dim <= 2^24 keeps a sequence's taps (W-1 rows) addressable with 32-bit offsets
+  if (d->n_seqs < (fwd ? 1 : 0) || d->dim < 8 || d->dim % 8 || d->dim > (1 << 24))
+    return KDA_ERR_SHAPE;
   const int64_t rows = fwd ? d->t_total : d->n_seqs;
   if (rows < 0 || rows > INT32_MAX) return KDA_ERR_SHAPE;
   if (d->state_indices && d->n_slots < 1) return KDA_ERR_SHAPE;
@@ -185,7 +187,7 @@ int check_conv(const kda_conv_desc* d, bool fwd, kda::ConvArgs* a) {
   // workgroups the launches need (one per 16-byte channel vector group)
   const int64_t vn = d->dtype == KDA_DTYPE_BF16 ? 8 : 4;
   const int64_t ncb = (d->dim / vn + 255) / 256;
-  if ((rows + 15) / 16 * ncb + (int64_t)d->n_seqs * ncb > INT32_MAX) return KDA_ERR_SHAPE;
+  if ((rows + 15) / 16 * ncb + (int64_t)d->n_seqs * ncb > INT32_MAX) return KDA_ERR_SHAPE;  // >= the real count
 
   const bool work = rows > 0;
   if (!d->weight || (work && !d->x)) return KDA_ERR_NULL;

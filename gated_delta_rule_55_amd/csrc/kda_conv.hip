@@ -12,14 +12,16 @@
 // bf16) with W fused multiply-adds per element, so the design is about access
 // shape only:
 //   - a thread owns one 16-byte vector of channels (8 bf16 / 4 fp32) over a
-//     run of L consecutive tokens, issues all L row loads before using any,
-//     and slides a W-1 tap window through them in registers; a wave reads
-//     and writes 1 KB contiguous per token row;
+//     run of L = 32 consecutive tokens, issues all L row loads before using
+//     any, and slides a W-1 tap window through them in registers; a wave
+//     reads and writes 1 KB contiguous per token row; outputs are written
+//     with streaming (non-temporal) stores;
 //   - the W-1 rows before a run are read again by the run's thread (halo);
 //     workgroup ids are remapped so that the runs of neighbouring tokens are
 //     handled on the same XCD, where that re-read hits the XCD's L2;
 //   - sequence boundaries depend on the token only, so the walk over
-//     cu_seqlens is uniform across a workgroup.
+//     cu_seqlens is uniform across a workgroup; a run inside one sequence
+//     (all runs but those meeting a boundary) has no per-token control flow.
 // The new taps are written by a second launch after every output row is
 // done, so an in-place state is never replaced while a run still reads it.
 #include <hip/hip_runtime.h>
@@ -31,7 +33,7 @@ namespace kda {
 namespace {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvRun = 16;  // tokens per thread in the forward
+constexpr int kConvRun = 32;  // tokens per thread in the forward
 
 template <typename T>
 struct CVec;  // 16 bytes of T
@@ -53,6 +55,12 @@ __device__ __forceinline__ typename CVec<T>::type load16(const T* p) {
 template <typename T>
 __device__ __forceinline__ void store16(T* p, typename CVec<T>::type v) {
   *reinterpret_cast<typename CVec<T>::type*>(p) = v;
+}
+// Streaming store: the forward's outputs are far larger than the caches and
+// are next read by another kernel, so they are written without keeping them.
+template <typename T>
+__device__ __forceinline__ void store16_stream(T* p, typename CVec<T>::type v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<typename CVec<T>::type*>(p));
 }
 
 // Blocks are dealt to the 8 XCDs round-robin by id; give each XCD a
@@ -123,12 +131,24 @@ struct Taps {
   float w[W][VN];
   float b[VN];
 
+  // The VN * W weights of channels c0 .. c0+VN-1 are consecutive and 16-byte
+  // aligned (c0 is a multiple of 4): VN * W / 4 vector loads.  The bias is
+  // read through a buffer resource that is empty when there is no bias.
   __device__ __forceinline__ void load(const ConvParams& p, int c0) {
+    const f32x4* wp = reinterpret_cast<const f32x4*>(p.weight + (int64_t)c0 * W);
 #pragma unroll
-    for (int e = 0; e < VN; ++e) {
+    for (int q = 0; q < VN * W / 4; ++q) {
+      const f32x4 v = wp[q];
 #pragma unroll
-      for (int j = 0; j < W; ++j) w[j][e] = p.weight[(int64_t)(c0 + e) * W + j];
-      b[e] = p.bias ? p.bias[c0 + e] : 0.f;
+      for (int m = 0; m < 4; ++m) w[(4 * q + m) % W][(4 * q + m) / W] = v[m];
+    }
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(const_cast<float*>(p.bias), p.bias ? p.dim * 4 : 0);
+#pragma unroll
+    for (int q = 0; q < VN / 4; ++q) {
+      const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, (c0 + 4 * q) * 4, 0, 0));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) b[4 * q + m] = v[m];
     }
   }
   // y for the current token from the W-1 window entries and the input xt
@@ -147,23 +167,54 @@ struct Taps {
   }
 };
 
-// Input at position pos of a sequence starting at s that carries `slot`'s taps.
+template <typename T>
+__device__ __forceinline__ typename CVec<T>::type buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(typename CVec<T>::type, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// The carried taps of `slot` as a buffer resource: W-1 rows of dim values,
+// or an empty buffer (every read gives 0) when there is no state or the
+// sequence is skipped.  Reads through it need no branch.
 template <typename T, int W>
-__device__ __forceinline__ void fetch(const ConvParams& p, int c0, int pos, int s, int slot,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t taps_rsrc(const ConvParams& p, int slot) {
+  const bool ok = p.state_in && slot >= 0;
+  const T* base = reinterpret_cast<const T*>(p.state_in) + (ok ? (int64_t)slot * (W - 1) * p.dim : 0);
+  return make_rsrc(const_cast<T*>(base), ok ? (W - 1) * p.dim * (int)sizeof(T) : 0);
+}
+
+// Rows lo .. hi-1 of x as a buffer resource (empty when hi <= lo, and then
+// never dereferenced, so x may be NULL).  At most W-1 rows are ever covered.
+template <typename T>
+struct XRows {
+  __amdgpu_buffer_rsrc_t r;
+  int lo;
+};
+template <typename T>
+__device__ __forceinline__ XRows<T> x_rows(const ConvParams& p, int lo, int hi) {
+  const T* base = reinterpret_cast<const T*>(p.x) + (int64_t)lo * p.dim;
+  return XRows<T>{make_rsrc(const_cast<T*>(base), hi > lo ? (hi - lo) * p.dim * (int)sizeof(T) : 0), lo};
+}
+
+// Input at position pos of a sequence starting at s: x[pos] when pos >= s
+// (read through xr, which covers the rows that can be asked for), else
+// carried tap pos - s + W - 1 (0 before the first tap).  Both candidates are
+// read through buffer resources, out-of-range reads give 0, and one is
+// selected: no load sits behind a branch.
+template <typename T, int W>
+__device__ __forceinline__ void fetch(const ConvParams& p, __amdgpu_buffer_rsrc_t taps,
+                                      const XRows<T>& xr, int c0, int pos, int s,
                                       float (&out)[CVec<T>::n]) {
   constexpr int VN = CVec<T>::n;
-  typename CVec<T>::type v;
+  constexpr int ES = (int)sizeof(T);
   const int tap = pos - s + (W - 1);
-  if (pos >= s) {
-    v = load16(reinterpret_cast<const T*>(p.x) + (int64_t)pos * p.dim + c0);
-  } else if (p.state_in && slot >= 0 && tap >= 0) {
-    v = load16(reinterpret_cast<const T*>(p.state_in) + ((int64_t)slot * (W - 1) + tap) * p.dim + c0);
-  } else {
+  const bool in_x = pos >= s;
+  const int toff = (!in_x && tap >= 0) ? (tap * p.dim + c0) * ES : kBufferOff;
+  const int xoff = (in_x && pos >= xr.lo && pos - xr.lo < W - 1) ? ((pos - xr.lo) * p.dim + c0) * ES
+                                                                   : kBufferOff;
+  const typename CVec<T>::type vs = buffer_load16<T>(taps, toff);
+  const typename CVec<T>::type vx = buffer_load16<T>(xr.r, xoff);
 #pragma unroll
-    for (int e = 0; e < VN; ++e) v[e] = from_f32<T>(0.f);
-  }
-#pragma unroll
-  for (int e = 0; e < VN; ++e) out[e] = to_f32(v[e]);
+  for (int e = 0; e < VN; ++e) out[e] = to_f32(in_x ? vx[e] : vs[e]);
 }
 
 template <typename T, int W, bool SILU>
@@ -178,7 +229,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(ConvParams p, in
   const int t0 = tb * L, t1 = min(t0 + L, p.rows);
   const T* x = reinterpret_cast<const T*>(p.x);
 
-  // every row of the run is requested before any is used
+  // every row of the run is requested before anything else
   V xr[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) xr[i] = load16(x + (int64_t)min(t0 + i, p.rows - 1) * p.dim + c0);
@@ -200,33 +251,65 @@ __global__ __launch_bounds__(kConvThreads) void conv_fwd_kernel(ConvParams p, in
   int s, e;
   seq_range(p, n, s, e);
   int slot = slot_of(p, n);
-
   float win[W - 1][VN];
-#pragma unroll
-  for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, c0, t0 - (W - 1) + j, s, slot, win[j]);
 
+  if (t0 >= s && t1 <= e) {
+    // The whole run lies in sequence n (every run but those that meet a
+    // sequence boundary): no per-token control flow.
+    if (slot < 0) return;
+    {
+      const XRows<T> xw = x_rows<T>(p, max(t0 - (W - 1), 0), t0);
+      const __amdgpu_buffer_rsrc_t tr = taps_rsrc<T, W>(p, slot);
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const int t = t0 + i;
-    if (t >= t1) break;
+      for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, tr, xw, c0, t0 - (W - 1) + j, s, win[j]);
+    }
+    const int len = t1 - t0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if (i < len)
+        store16_stream(oc.base + (int64_t)(t0 + i) * oc.ld, taps.template apply<SILU>(win, xr[i]));
+#pragma unroll
+      for (int j = 0; j < W - 2; ++j)
+#pragma unroll
+        for (int v = 0; v < VN; ++v) win[j][v] = win[j + 1][v];
+#pragma unroll
+      for (int v = 0; v < VN; ++v) win[W - 2][v] = to_f32(xr[i][v]);
+    }
+    return;
+  }
+
+  // A run that meets a sequence boundary: token by token, re-reading each
+  // row (it was just fetched above, so from cache).
+  {
+    const XRows<T> xw = x_rows<T>(p, max(t0 - (W - 1), 0), t0);
+    const __amdgpu_buffer_rsrc_t tr = taps_rsrc<T, W>(p, slot);
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, tr, xw, c0, t0 - (W - 1) + j, s, win[j]);
+  }
+#pragma unroll 1
+  for (int t = t0; t < t1; ++t) {
     if (t >= e && n < p.n_seqs - 1) {
       do {
         ++n;
         seq_range(p, n, s, e);
       } while (t >= e && n < p.n_seqs - 1);
       slot = slot_of(p, n);
-    }
-    if (t == s) {  // first token of a sequence: the window is its carried taps
+      if (t == s) {  // first token of a sequence: the window is its carried taps
+        const __amdgpu_buffer_rsrc_t tr = taps_rsrc<T, W>(p, slot);
+        const XRows<T> none = x_rows<T>(p, 0, 0);
 #pragma unroll
-      for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, c0, t - (W - 1) + j, s, slot, win[j]);
+        for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, tr, none, c0, t - (W - 1) + j, s, win[j]);
+      }
     }
-    if (t >= s && t < e && slot >= 0) store16(oc.base + (int64_t)t * oc.ld, taps.template apply<SILU>(win, xr[i]));
+    const V xt = load16(x + (int64_t)t * p.dim + c0);
+    if (t >= s && t < e && slot >= 0)
+      store16_stream(oc.base + (int64_t)t * oc.ld, taps.template apply<SILU>(win, xt));
 #pragma unroll
     for (int j = 0; j < W - 2; ++j)
 #pragma unroll
       for (int v = 0; v < VN; ++v) win[j][v] = win[j + 1][v];
 #pragma unroll
-    for (int v = 0; v < VN; ++v) win[W - 2][v] = to_f32(xr[i][v]);
+    for (int v = 0; v < VN; ++v) win[W - 2][v] = to_f32(xt[v]);
   }
 }
 
@@ -245,9 +328,11 @@ __global__ __launch_bounds__(kConvThreads) void conv_state_kernel(ConvParams p, 
   const int c0 = cv * VN;
   int s, e;
   seq_range(p, n, s, e);
+  const __amdgpu_buffer_rsrc_t tr = taps_rsrc<T, W>(p, slot);
+  const XRows<T> xw = x_rows<T>(p, max(e - (W - 1), s), e);
   float tap[W - 1][VN];
 #pragma unroll
-  for (int i = 0; i < W - 1; ++i) fetch<T, W>(p, c0, e - (W - 1) + i, s, slot, tap[i]);
+  for (int i = 0; i < W - 1; ++i) fetch<T, W>(p, tr, xw, c0, e - (W - 1) + i, s, tap[i]);
   T* out = reinterpret_cast<T*>(p.state_out) + (int64_t)slot * (W - 1) * p.dim + c0;
 #pragma unroll
   for (int i = 0; i < W - 1; ++i) {
@@ -270,9 +355,10 @@ __global__ __launch_bounds__(kConvThreads) void conv_update_kernel(ConvParams p,
   if (slot < 0) return;
   const int c0 = cv * VN;
   const V xt = load16(reinterpret_cast<const T*>(p.x) + (int64_t)n * p.dim + c0);
+  const __amdgpu_buffer_rsrc_t tr = taps_rsrc<T, W>(p, slot);
   float win[W - 1][VN];
 #pragma unroll
-  for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, c0, j - (W - 1), 0, slot, win[j]);
+  for (int j = 0; j < W - 1; ++j) fetch<T, W>(p, tr, x_rows<T>(p, 0, 0), c0, j - (W - 1), 0, win[j]);
   Taps<T, W> taps;
   taps.load(p, c0);
   const OutCol<T> oc = out_col<T>(p, c0);

@@ -67,7 +67,7 @@ typedef struct {
   uint32_t struct_size;         /* sizeof(kda_conv_desc)                        */
   int32_t dtype;                /* kda_dtype of x, y and the state              */
   int32_t n_seqs;               /* N: >= 1 for the forward, >= 0 for update    */
-  int32_t dim;                  /* channels, a positive multiple of 8           */
+  int32_t dim;                  /* channels, a multiple of 8, 8 .. 2^24         */
   int32_t width;                /* W in {2, 3, 4}; 0 = 4                        */
   int32_t activation;           /* kda_conv_act                                 */
   int64_t t_total;              /* forward: packed tokens (>= 0); update: unused */
