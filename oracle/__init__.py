@@ -8,8 +8,10 @@ it.  Contents:
   chunked.py                    fp64 chunked re-derivation of the same result
   gate.py                       the Kimi gate activation (fp64)
   conv.py                       short causal conv with carried taps (fp64)
+  heads.py                      q/k L2 normalisation, grouped key heads (fp64)
 """
 from .recurrent import OracleLib, decode, lib_path, num_threads, prefill  # noqa: F401
 from .chunked import chunked_prefill, unit_lower_inverse  # noqa: F401
 from .gate import kimi_gate, softplus  # noqa: F401
 from .conv import causal_conv1d, silu  # noqa: F401
+from .heads import L2NORM_EPS, expand_key_heads, l2norm  # noqa: F401
