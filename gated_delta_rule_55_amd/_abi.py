@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
-KDA_ABI_VERSION = 3
+KDA_ABI_VERSION = 4
 KDA_OK = 0
 KDA_ERR_NULL = -1
 KDA_ERR_SHAPE = -2
@@ -69,6 +69,8 @@ class PrefillDesc(ctypes.Structure):
         ("gate", GateDesc),
         ("state_indices", ctypes.c_void_p),
         ("n_slots", ctypes.c_int32),
+        ("n_k_heads", ctypes.c_int32),
+        ("qk_l2norm", ctypes.c_int32),
     ]
 
 
@@ -91,6 +93,8 @@ class DecodeDesc(ctypes.Structure):
         ("gate", GateDesc),
         ("state_indices", ctypes.c_void_p),
         ("n_slots", ctypes.c_int32),
+        ("n_k_heads", ctypes.c_int32),
+        ("qk_l2norm", ctypes.c_int32),
     ]
 
 

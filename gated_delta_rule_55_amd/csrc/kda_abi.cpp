@@ -39,6 +39,16 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.l
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 
+// Key heads (0 = H, else a divisor of H) and the q/k normalisation flag.
+int check_qk(int32_t n_k_heads, int32_t qk_l2norm, int H, kda::QkArgs* out) {
+  const int hg = n_k_heads == 0 ? H : n_k_heads;
+  if (hg < 1 || hg > H || H % hg != 0) return KDA_ERR_SHAPE;
+  if (qk_l2norm != 0 && qk_l2norm != 1) return KDA_ERR_UNSUPPORTED;
+  out->kheads = hg;
+  out->norm = qk_l2norm;
+  return KDA_OK;
+}
+
 // The decay input of a descriptor: g (fp32), or the raw gate x (element size
 // es) with a_log [H] and dt_bias [H, D].  `rows` = tokens (prefill) or
 // sequences (decode).  Fills the ranges the call reads.
@@ -94,6 +104,8 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
   // run of it left a GPU unusable without an explained cause.  It stays
   // rejected here, before anything is launched, until that is understood.
   if (chunked && d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
+  const int sq = check_qk(d->n_k_heads, d->qk_l2norm, d->n_heads, &a->qk);
+  if (sq != KDA_OK) return sq;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
   a->plan = d->plan;
   a->n_seqs = d->n_seqs;
@@ -138,7 +150,8 @@ int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range
   Range rgate[3];
   const int st = check_gate(d->gate, d->g, T > 0, T, H, D, es, &a->gate, rgate);
   if (st != KDA_OK) return st;
-  const Range rq = range_of(d->q, T * H * D * es), rk = range_of(d->k, T * H * D * es),
+  const int64_t HG = a->qk.kheads;
+  const Range rq = range_of(d->q, T * HG * D * es), rk = range_of(d->k, T * HG * D * es),
               rv = range_of(d->v, T * H * D * es), rb = range_of(d->beta, T * H * es),
               ro = range_of(d->o, T * H * D * es),
               rh0 = range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
@@ -337,6 +350,9 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   if (!std::isfinite(d->scale)) return KDA_ERR_SHAPE;
   if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
   if (d->state_indices && d->n_slots < 1) return KDA_ERR_SHAPE;
+  kda::DecodeArgs a;
+  const int sq = check_qk(d->n_k_heads, d->qk_l2norm, d->n_heads, &a.qk);
+  if (sq != KDA_OK) return sq;
   if (d->n_seqs == 0) return KDA_OK;
   if (!d->state || !d->q || !d->k || !d->v || !d->beta || !d->o) return KDA_ERR_NULL;
   const bool bf = d->dtype == KDA_DTYPE_BF16;
@@ -347,14 +363,14 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   for (const void* p : pe)
     if (!aligned(p, bf ? 2 : 4)) return KDA_ERR_ALIGN;
   const int64_t es = bf ? 2 : 4, NH = (int64_t)d->n_seqs * d->n_heads, D = d->dk;
-  kda::DecodeArgs a;
+  const int64_t NHG = (int64_t)d->n_seqs * a.qk.kheads;
   Range rgate[3];
   const int st = check_gate(d->gate, d->g, true, d->n_seqs, d->n_heads, D, es, &a.gate, rgate);
   if (st != KDA_OK) return st;
   const Range ro = range_of(d->o, NH * D * es);
   const int64_t NS = (d->state_indices ? (int64_t)d->n_slots : (int64_t)d->n_seqs) * d->n_heads;
-  const Range ins[] = {range_of(d->state, NS * D * D * 4), range_of(d->q, NH * D * es),
-                       range_of(d->k, NH * D * es),        range_of(d->v, NH * D * es),
+  const Range ins[] = {range_of(d->state, NS * D * D * 4), range_of(d->q, NHG * D * es),
+                       range_of(d->k, NHG * D * es),       range_of(d->v, NH * D * es),
                        rgate[0], rgate[1], rgate[2],       range_of(d->beta, NH * es),
                        range_of(d->state_indices, d->state_indices ? (int64_t)d->n_seqs * 4 : 0)};
   for (const Range& r : ins)

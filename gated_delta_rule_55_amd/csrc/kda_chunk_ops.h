@@ -101,7 +101,8 @@ struct Geo {
   static constexpr size_t OFF_FAC = OFF_RHO + (size_t)(TT + 1) * D * 4;
   static constexpr size_t OFF_BETA = OFF_FAC + (size_t)NFAC * D * 4;
   static constexpr size_t OFF_FLAG = OFF_BETA + (size_t)C * 4;
-  static constexpr size_t LOCAL_LDS = align_up(OFF_FLAG + 16, 16);
+  static constexpr size_t OFF_NRM = OFF_FLAG + 16;  // [2][C]: 1/|k_r|, 1/|q_r|
+  static constexpr size_t LOCAL_LDS = align_up(OFF_NRM + (size_t)2 * C * 4, 16);
 
   // Scan-step LDS (aliases the chunk-local region; the two never overlap).
   static constexpr int VT_LD = KCP + TP;
@@ -175,6 +176,14 @@ struct DecayIn {
   const float* dt_bias;
 };
 
+// Key heads and q/k normalisation: q and k rows hold kheads heads, value
+// head h reads key head h / (n_heads / kheads); norm = 1 divides each q and k
+// row by sqrt(sum of squares + kQkNormEps) when it is staged.
+struct QkIn {
+  int kheads;
+  int norm;
+};
+
 template <typename TIO, int D, int C, bool GATE = false>
 struct ChunkLocal {
   using Gm = Geo<TIO, D, C>;
@@ -210,15 +219,51 @@ struct ChunkLocal {
     return uint4{a.x & mk, a.y & mk, a.z & mk, a.w & mk};
   }
 
+  // Divide the row that VPR consecutive lanes hold (one 16-byte vector each)
+  // by sqrt(sum of squares + eps); returns the factor.  Every lane of the
+  // wave must call it.
+  static __device__ __forceinline__ float normalise_row(uint4& u) {
+    float f[EPV];
+    if constexpr (EPV == 8) {
+      const bf16x8 b = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = (float)b[e];
+    } else {
+      const f32x4 b = __builtin_bit_cast(f32x4, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = b[e];
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) ss += f[e] * f[e];
+#pragma unroll
+    for (int o = 1; o < VPR; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    const float r = __builtin_amdgcn_rsqf(ss + kQkNormEps);
+    if constexpr (EPV == 8) {
+      bf16x8 b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = (bf16)(f[e] * r);
+      u = __builtin_bit_cast(uint4, b);
+    } else {
+      f32x4 b;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = f[e] * r;
+      u = __builtin_bit_cast(uint4, b);
+    }
+    return r;
+  }
+
   // Issue every global load of one (chunk, head); nothing waits on them here.
   static __device__ __forceinline__ void prefetch(Inputs& in, const TIO* __restrict__ q,
                                                   const TIO* __restrict__ k,
                                                   const TIO* __restrict__ v,
                                                   const DecayIn<TIO>& dec,
                                                   const TIO* __restrict__ beta, int n_heads,
-                                                  int h, int64_t tok0, int L) {
+                                                  int h, int64_t tok0, int L, QkIn qk) {
     const int tid = threadIdx.x;
     const int64_t rs = (int64_t)n_heads * D;
+    const int64_t ks = (int64_t)qk.kheads * D;                      // q / k row stride
+    const int64_t kh = (int64_t)(h / (n_heads / qk.kheads)) * D;    // key head offset
     in.tok0 = tok0;
     in.len = L;
 #pragma unroll
@@ -227,8 +272,9 @@ struct ChunkLocal {
       const int x = x0 < C * VPR ? x0 : C * VPR - 1;
       const int r = min(x / VPR, L - 1), cv = x % VPR;
       const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
-      in.k[m] = reinterpret_cast<const uint4*>(k + off)[cv];
-      in.q[m] = reinterpret_cast<const uint4*>(q + off)[cv];
+      const int64_t koff = (tok0 + r) * ks + kh;
+      in.k[m] = reinterpret_cast<const uint4*>(k + koff)[cv];
+      in.q[m] = reinterpret_cast<const uint4*>(q + koff)[cv];
       in.v[m] = reinterpret_cast<const uint4*>(v + off)[cv];
     }
 #pragma unroll
@@ -251,13 +297,16 @@ struct ChunkLocal {
   // Entry-by-entry Gram tile from the inputs in global memory, for a diagonal
   // tile whose decay span is too large to factor.  Lane holds rows
   // 16a + 4lg + j, column 16a + l16 (accumulator layout).
+  // With q/k normalisation, nrm holds the row factors (1/|k_r| then 1/|q_r|).
   static __device__ void exact_diag_tile(int a, f32x4& akk, f32x4& aqk,
                                          const TIO* __restrict__ q, const TIO* __restrict__ k,
                                          const DecayIn<TIO>& dec, float ea, int n_heads, int h,
-                                         int64_t tok0, int L) {
+                                         int64_t tok0, int L, QkIn qk, const float* nrm) {
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, lg = lane >> 4;
     const int64_t rs = (int64_t)n_heads * D;
+    const int64_t ks = (int64_t)qk.kheads * D;
+    const int64_t kh = (int64_t)(h / (n_heads / qk.kheads)) * D;
     const int ii = 16 * a + l16;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -274,9 +323,13 @@ struct ChunkLocal {
               e += dec.g[at] * kLog2e;
           }
           const float f = fast_exp2(e);
-          const float ki = to_f32(k[(tok0 + ii) * rs + (int64_t)h * D + c]) * f;
-          sk += to_f32(k[(tok0 + rr) * rs + (int64_t)h * D + c]) * ki;
-          sq += to_f32(q[(tok0 + rr) * rs + (int64_t)h * D + c]) * ki;
+          const float ki = to_f32(k[(tok0 + ii) * ks + kh + c]) * f;
+          sk += to_f32(k[(tok0 + rr) * ks + kh + c]) * ki;
+          sq += to_f32(q[(tok0 + rr) * ks + kh + c]) * ki;
+        }
+        if (qk.norm) {
+          sk *= nrm[rr] * nrm[ii];
+          sq *= nrm[C + rr] * nrm[ii];
         }
       }
       akk[j] = sk;
@@ -312,7 +365,7 @@ struct ChunkLocal {
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
                              ChunkOut<TIO> out, const TIO* __restrict__ q,
                              const TIO* __restrict__ k, const DecayIn<TIO>& dec, int n_heads,
-                             int h) {
+                             int h, QkIn qk) {
     float* Gs = reinterpret_cast<float*>(lds + Gm::OFF_GS);
     float* As = reinterpret_cast<float*>(lds + Gm::OFF_AS);
     float* Ts = reinterpret_cast<float*>(lds + Gm::OFF_TS);
@@ -329,6 +382,7 @@ struct ChunkLocal {
     float* fac = reinterpret_cast<float*>(lds + Gm::OFF_FAC);  // [NFAC][D]
     float* s_beta = reinterpret_cast<float*>(lds + Gm::OFF_BETA);
     int* s_flag = reinterpret_cast<int*>(lds + Gm::OFF_FLAG);
+    float* s_nrm = reinterpret_cast<float*>(lds + Gm::OFF_NRM);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -347,11 +401,19 @@ struct ChunkLocal {
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int x = tid + NT * m;
+      uint4 kv = in.k[m], qv = in.q[m];
+      if (qk.norm) {  // the VPR lanes holding a row reduce its sum of squares
+        const float fk = normalise_row(kv), fq = normalise_row(qv);
+        if (x < C * VPR && x % VPR == 0) {
+          s_nrm[x / VPR] = fk;
+          s_nrm[C + x / VPR] = fq;
+        }
+      }
       if (x < C * VPR) {
         const int r = x / VPR, cv = x % VPR;
         const unsigned mk = r < in.len ? ~0u : 0u;
-        reinterpret_cast<uint4*>(Lk + r * KS_LD)[cv] = mask4(in.k[m], mk);
-        reinterpret_cast<uint4*>(Lq + r * KS_LD)[cv] = mask4(in.q[m], mk);
+        reinterpret_cast<uint4*>(Lk + r * KS_LD)[cv] = mask4(kv, mk);
+        reinterpret_cast<uint4*>(Lq + r * KS_LD)[cv] = mask4(qv, mk);
         reinterpret_cast<uint4*>(Vs + r * KS_LD)[cv] = mask4(in.v[m], mk);
       }
     }
@@ -492,7 +554,7 @@ struct ChunkLocal {
         }
         f32x4 akk = zero4(), aqk = zero4();
         if (a == b && (flag >> a) & 1) {
-          exact_diag_tile(a, akk, aqk, q, k, dec, in.ea, n_heads, h, in.tok0, in.len);
+          exact_diag_tile(a, akk, aqk, q, k, dec, in.ea, n_heads, h, in.tok0, in.len, qk, s_nrm);
         } else {
           const TIO* lkr = Lk + (16 * a + l16) * KS_LD;
           const TIO* lqr = Lq + (16 * a + l16) * KS_LD;

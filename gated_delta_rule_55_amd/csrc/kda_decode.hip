@@ -23,6 +23,35 @@
 
 namespace kda {
 
+// One wave: k . q and, when the rows are to be L2-normalised, the factors
+// 1/sqrt(|k|^2 + eps) and 1/sqrt(|q|^2 + eps) (else 1).  The kernels use the
+// raw rows and apply the factors to the reductions they feed: k . q, S^T k,
+// S^T q and the rank-one write k u^T.
+template <int D>
+__device__ __forceinline__ void qk_dots(const float* sk, const float* sq, int norm, float* kq,
+                                        float* rk, float* rq) {
+  const int lane = threadIdx.x & 63;
+  float a = 0.f, kk = 0.f, qq = 0.f;
+  for (int i = lane; i < D; i += 64) {
+    a += sk[i] * sq[i];
+    kk += sk[i] * sk[i];
+    qq += sq[i] * sq[i];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    kk += __shfl_xor(kk, off, 64);
+    qq += __shfl_xor(qq, off, 64);
+  }
+  if (lane == 0) {
+    const float fk = norm ? __builtin_amdgcn_rsqf(kk + kQkNormEps) : 1.f;
+    const float fq = norm ? __builtin_amdgcn_rsqf(qq + kQkNormEps) : 1.f;
+    *kq = a * fk * fq;
+    *rk = fk;
+    *rq = fq;
+  }
+}
+
 // GATE: the decay comes from the raw gate x with a_log and dt_bias (the Kimi
 // gate, see kimi_gate_log2) instead of a given g.
 template <typename TIO, int D, bool GATE>
@@ -36,7 +65,8 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
                                                      const float* __restrict__ dt_bias,
                                                      int n_heads, const TIO* __restrict__ beta,
                                                      TIO* __restrict__ o, float scale,
-                                                     const int* __restrict__ slots, int n_slots) {
+                                                     const int* __restrict__ slots, int n_slots,
+                                                     int kheads, int qk_norm) {
   constexpr int NQ = D / 4;       // column quads per row
   constexpr int RG = 256 / NQ;    // row groups
   constexpr int RPT = D / RG;     // rows per thread
@@ -44,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 
   __shared__ float s_q[D], s_k[D], s_d[D], s_u[D];
   __shared__ float s_red[2][RG][D];
-  __shared__ float s_kq;
+  __shared__ float s_kq, s_rk, s_rq;  // k.q (normalised), 1/|k|, 1/|q| (1 without norm)
 
   const int tid = threadIdx.x;
   const int cq = tid % NQ;
@@ -66,9 +96,11 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   for (int i = 0; i < RPT; ++i)
     s[i] = *reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + 4 * cq);
 
+  // key head of value head h: h / (n_heads / kheads), rows of kheads heads
+  const int64_t qk_row = (nh / n_heads) * kheads + (nh % n_heads) / (n_heads / kheads);
   if (tid < D) {
-    s_q[tid] = to_f32(q[nh * D + tid]);
-    s_k[tid] = to_f32(k[nh * D + tid]);
+    s_q[tid] = to_f32(q[qk_row * D + tid]);
+    s_k[tid] = to_f32(k[qk_row * D + tid]);
     if constexpr (GATE) {
       const int h = (int)(nh % n_heads);
       s_d[tid] = fast_exp2(kimi_gate_log2(to_f32(gx[nh * D + tid]) + dt_bias[h * D + tid],
@@ -78,13 +110,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
     }
   }
   __syncthreads();
-  if (tid < 64) {  // k . q by one wave
-    float acc = 0.f;
-    for (int i = tid; i < D; i += 64) acc += s_k[i] * s_q[i];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (tid == 0) s_kq = acc;
-  }
+  if (tid < 64) qk_dots<D>(s_k, s_q, qk_norm, &s_kq, &s_rk, &s_rq);
 
   f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
@@ -105,6 +131,8 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
       p += s_red[0][j][tid];
       r += s_red[1][j][tid];
     }
+    p *= s_rk;
+    r *= s_rq;
     const float b = to_f32(beta[nh]);
     const float u = b * (to_f32(v[nh * D + tid]) - p);
     s_u[tid] = u;
@@ -112,7 +140,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   }
   __syncthreads();
 
-  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
+  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]) * s_rk;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
@@ -137,7 +165,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const TIO* __restrict__ gx, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, const TIO* __restrict__ beta, TIO* __restrict__ o,
     float scale, int n_heads, int64_t t_total, const int* __restrict__ cu,
-    const int* __restrict__ slots, int n_slots) {
+    const int* __restrict__ slots, int n_slots, int kheads, int qk_norm) {
   constexpr int NQ = D / 4;
   constexpr int RG = 256 / NQ;
   constexpr int RPT = D / RG;
@@ -145,7 +173,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
 
   __shared__ float s_q[2][D], s_k[2][D], s_d[2][D], s_v[2][D], s_u[D];
   __shared__ float s_red[2][RG][D];
-  __shared__ float s_kq, s_b[2];
+  __shared__ float s_kq, s_rk, s_rq, s_b[2];
 
   const int tid = threadIdx.x;
   const int cq = tid % NQ;
@@ -171,11 +199,13 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   // this thread's element of one token (tid < D), loaded ahead
   TIO rq{}, rk{}, rv{}, rx{}, rb{};
   float rg_{};
+  const int kh = h / (n_heads / kheads);  // key head of value head h
   auto fetch = [&](int64_t t) {
     if (tid < D) {
       const int64_t at = (t * n_heads + h) * D + tid;
-      rq = q[at];
-      rk = k[at];
+      const int64_t akt = (t * kheads + kh) * D + tid;
+      rq = q[akt];
+      rk = k[akt];
       rv = v[at];
       if constexpr (GATE) rx = gx[at];
       else rg_ = g[at];
@@ -195,13 +225,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     if (tid == 0) s_b[pb] = to_f32(rb);
     __syncthreads();
     if (t + 1 < t1) fetch(t + 1);
-    if (tid < 64) {  // k . q by one wave
-      float acc = 0.f;
-      for (int i = tid; i < D; i += 64) acc += s_k[pb][i] * s_q[pb][i];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-      if (tid == 0) s_kq = acc;
-    }
+    if (tid < 64) qk_dots<D>(s_k[pb], s_q[pb], qk_norm, &s_kq, &s_rk, &s_rq);
     f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -220,12 +244,14 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
         p += s_red[0][j][tid];
         r += s_red[1][j][tid];
       }
+      p *= s_rk;
+      r *= s_rq;
       const float u = s_b[pb] * (s_v[pb][tid] - p);
       s_u[tid] = u;
       o[(t * n_heads + h) * D + tid] = from_f32<TIO>(scale * (r + s_kq * u));
     }
     __syncthreads();
-    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
+    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]) * s_rk;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rg + RG * i;
@@ -247,13 +273,13 @@ static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream)
                        stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
                        a.g, (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias,
                        (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
-                       a.cu_seqlens, a.slots, a.n_slots);
+                       a.cu_seqlens, a.slots, a.n_slots, a.qk.kheads, a.qk.norm);
   else
     hipLaunchKernelGGL((recurrent_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0,
                        stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
                        a.g, (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
                        (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
-                       a.cu_seqlens, a.slots, a.n_slots);
+                       a.cu_seqlens, a.slots, a.n_slots, a.qk.kheads, a.qk.norm);
   return hipGetLastError();
 }
 
@@ -279,12 +305,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((decode_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0, stream,
                        a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias, a.n_heads,
-                       (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots);
+                       (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots, a.qk.kheads,
+                       a.qk.norm);
   else
     hipLaunchKernelGGL((decode_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0, stream,
                        a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
-                       a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots);
+                       a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots,
+                       a.qk.kheads, a.qk.norm);
   return hipGetLastError();
 }
 

@@ -131,6 +131,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// eps of the in-kernel q / k L2 normalisation: x / sqrt(sum x^2 + eps).
+constexpr float kQkNormEps = 1e-6f;
+
 // The Kimi gate in base 2: g log2(e) with g = -exp(a_log) softplus(z),
 // z = x + dt_bias, given ea = exp(a_log).  softplus(z) log2(e) =
 // log2(1 + 2^(z log2 e)), which is z log2(e) to fp32 precision once that

@@ -20,9 +20,18 @@ struct GateArgs {
   const float* dt_bias = nullptr;
 };
 
+// Key/query heads and their normalisation: q and k rows hold kheads heads;
+// value head h reads key head h / (n_heads / kheads); norm = 1 divides each
+// q and k row by sqrt(sum of squares + 1e-6) before use.
+struct QkArgs {
+  int kheads = 0;  // Hg (== n_heads when not grouped)
+  int norm = 0;
+};
+
 struct DecodeArgs {
   bool bf16;
   int n_seqs, n_heads, d;
+  QkArgs qk;
   float scale;
   float* state;
   const void *q, *k, *v;
@@ -42,6 +51,7 @@ constexpr int KDA_PLAN_TWO_PASS_ = 2;
 struct PrefillArgs {
   bool bf16;
   int n_seqs, n_heads, d, chunk, plan;
+  QkArgs qk;
   int64_t t_total;
   float scale;
   const void *q, *k, *v;

@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 template <typename TIO, int D, int C, bool GATE>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
-    DecayIn<TIO> dec, const TIO* __restrict__ beta, int n_heads, float scale,
+    DecayIn<TIO> dec, const TIO* __restrict__ beta, int n_heads, QkIn qk, float scale,
     const int* __restrict__ chunk_total, const ChunkEnt* __restrict__ tab,
     unsigned char* __restrict__ blocks) {
   using CL = ChunkLocal<TIO, D, C, GATE>;
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
   const int n_items = *chunk_total * n_heads;
   auto fetch = [&](typename CL::Inputs& in, int w) {
     const ChunkEnt ent = tab[w / n_heads];
-    CL::prefetch(in, q, k, v, dec, beta, n_heads, w % n_heads, ent.start, ent.len);
+    CL::prefetch(in, q, k, v, dec, beta, n_heads, w % n_heads, ent.start, ent.len, qk);
   };
   auto compute = [&](const typename CL::Inputs& in, int w) {
     const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)w * Gm::OUT_BYTES);
-    CL::run(lds, in, scale, out, q, k, dec, n_heads, w % n_heads);
+    CL::run(lds, in, scale, out, q, k, dec, n_heads, w % n_heads, qk);
     __syncthreads();  // the next item overwrites the LDS
   };
   typename CL::Inputs cur, nxt;
@@ -305,6 +305,7 @@ struct FusedArgs {
   float* ht;
   void* o;
   int n_seqs, n_heads, nteams;
+  QkIn qk;
   float scale;
   int* status;
   const int* chunk_off;
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
     have_in = !pc.end;
     if (have_in) {
       const ChunkEnt ent = a.tab[pc.ci];
-      CL::prefetch(in, q, k, v, dec, beta, a.n_heads, pc.h, ent.start, ent.len);
+      CL::prefetch(in, q, k, v, dec, beta, a.n_heads, pc.h, ent.start, ent.len, a.qk);
     }
   };
   // Produce chunk ps from `in`, publish it, step to this member's next chunk
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
       if (!s_ok) return false;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    CL::run(lds, in, a.scale, slot_out(ps), q, k, dec, a.n_heads, pc.h);
+    CL::run(lds, in, a.scale, slot_out(ps), q, k, dec, a.n_heads, pc.h, a.qk);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // every wave's stores
     __syncthreads();
     if (tid == 0)
@@ -581,6 +582,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
       fa.o = a.o;
       fa.n_seqs = a.n_seqs;
       fa.n_heads = a.n_heads;
+      fa.qk = QkIn{a.qk.kheads, a.qk.norm};
       fa.nteams = nteams;
       fa.scale = a.scale;
       fa.status = status;
@@ -617,13 +619,13 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
     if (gate)
       hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, true>), dim3(grid), dim3(kLocalThreads),
                          Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
-                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads, a.scale,
-                         chunk_off + a.n_seqs, tab, blocks);
+                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
+                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks);
     else
       hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, false>), dim3(grid), dim3(kLocalThreads),
                          Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
-                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads, a.scale,
-                         chunk_off + a.n_seqs, tab, blocks);
+                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
+                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
     const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * (D / 16));

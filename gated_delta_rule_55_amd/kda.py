@@ -65,16 +65,16 @@ def _check_gate(gate, g, lead, H, dk, dtype, dev):
 
 def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
                  ht=None, plan="auto", gate=None, state_indices=None,
-                 n_slots=0) -> _abi.PrefillDesc:
-    T, H, dk = q.shape
-    dv = v.shape[-1]
+                 n_slots=0, qk_l2norm=False) -> _abi.PrefillDesc:
+    T, Hg, dk = q.shape
+    H, dv = v.shape[1], v.shape[-1]
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
     return _abi.prefill_desc(
         dtype=_DTYPES[q.dtype], n_seqs=N, n_heads=H, dk=dk, dv=dv, chunk=int(chunk),
         plan=_PLANS[plan], t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
         v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
         o=_ptr(o), ht=_ptr(ht), gate=_gate_tuple(gate), state_indices=_ptr(state_indices),
-        n_slots=int(n_slots))
+        n_slots=int(n_slots), n_k_heads=Hg, qk_l2norm=int(bool(qk_l2norm)))
 
 
 def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht, output_final_state, gate,
@@ -85,11 +85,15 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht, output_final_state,
         raise ValueError("the KDA prefill runs on the GPU only")
     if q.dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {q.dtype}")
-    T, H, dk = q.shape
-    dv = v.shape[-1]
+    T, Hg, dk = q.shape
+    if v.dim() != 3:
+        raise ValueError(f"v must be [T, H, dv], got {tuple(v.shape)}")
+    H, dv = int(v.shape[1]), int(v.shape[2])
+    if H % Hg:
+        raise ValueError(f"q/k heads {Hg} must divide the value heads {H}")
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
-    _check(q, "q", (T, H, dk), q.dtype, dev)
-    _check(k, "k", (T, H, dk), q.dtype, dev)
+    _check(q, "q", (T, Hg, dk), q.dtype, dev)
+    _check(k, "k", (T, Hg, dk), q.dtype, dev)
     _check(v, "v", (T, H, dv), q.dtype, dev)
     _check_gate(gate, g, (T,), H, dk, q.dtype, dev)
     _check(beta, "beta", (T, H), q.dtype, dev)
@@ -130,9 +134,10 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   output_final_state: bool = True, stream=None, events=None,
                   plan: str = "auto", gate=None,
-                  state_indices: Optional[torch.Tensor] = None
+                  state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked KDA prefill.  q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
+    """Chunked KDA prefill.  q, k: [T, Hg, dk] (Hg key heads, each shared by
+    H / Hg consecutive value heads; Hg = H by default); g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
     h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
     None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
     `ht` may be h0 itself (in-place carry).  `events`: four torch.cuda.Event
@@ -144,12 +149,13 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     fp32) to compute g = -exp(a_log) softplus(x + dt_bias) in the kernels
     (g may then be None).  `state_indices` (int32 [N] on the device): h0 and
     ht are then state pools [S, H, dk, dv] (ht defaults to h0: in place) and
-    sequence n uses slot state_indices[n]; a negative slot skips it."""
+    sequence n uses slot state_indices[n]; a negative slot skips it.
+    `qk_l2norm`: L2-normalise every q and k row in the kernels (eps 1e-6)."""
     dev = q.device
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
                                         output_final_state, gate, state_indices, None)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate,
-                        state_indices, n_slots)
+                        state_indices, n_slots, qk_l2norm)
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -168,7 +174,7 @@ def recurrent_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                       out: Optional[torch.Tensor] = None, ht: Optional[torch.Tensor] = None,
                       output_final_state: bool = True, stream=None, gate=None,
-                      state_indices: Optional[torch.Tensor] = None
+                      state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False
                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The prefill of chunk_prefill computed token by token with the state held
     on chip (for continuing prefills of a few tokens on a carried state).  Same
@@ -176,7 +182,7 @@ def recurrent_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
                                         output_final_state, gate, state_indices, None)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, 64, out, ht, "auto", gate,
-                        state_indices, n_slots)
+                        state_indices, n_slots, qk_l2norm)
     st = _abi.recurrent_prefill_raw(desc, _stream(stream))
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_recurrent_prefill")
@@ -186,9 +192,11 @@ def recurrent_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      g: Optional[torch.Tensor], beta: torch.Tensor, scale: Optional[float] = None,
                      out: Optional[torch.Tensor] = None, stream=None, gate=None,
-                     state_indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     state_indices: Optional[torch.Tensor] = None,
+                     qk_l2norm: bool = False) -> torch.Tensor:
     """One recurrent decode step; `state` [N, H, dk, dv] fp32 is updated in place.
-    q, k, g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].  Returns o [N, H, dv].
+    q, k: [N, Hg, dk] (Hg divides H); g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].
+    Returns o [N, H, dv].  `qk_l2norm` as in chunk_prefill.
     `gate` as in chunk_prefill (x is [N, H, dk]).  `state_indices` (int32 [N]
     on the device): `state` is then a pool [S, H, dk, dv] and sequence n
     updates slot state_indices[n]; a negative slot skips it (its o is left as
@@ -203,8 +211,11 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
     _check(state, "state", (S, H, dk, dv), torch.float32, dev)
     if state_indices is not None:
         _check(state_indices, "state_indices", (N,), torch.int32, dev)
-    _check(q, "q", (N, H, dk), q.dtype, dev)
-    _check(k, "k", (N, H, dk), q.dtype, dev)
+    Hg = int(q.shape[1]) if q.dim() == 3 else H
+    if Hg < 1 or H % Hg:
+        raise ValueError(f"q/k heads {Hg} must divide the value heads {H}")
+    _check(q, "q", (N, Hg, dk), q.dtype, dev)
+    _check(k, "k", (N, Hg, dk), q.dtype, dev)
     _check(v, "v", (N, H, dv), q.dtype, dev)
     _check_gate(gate, g, (N,), H, dk, q.dtype, dev)
     _check(beta, "beta", (N, H), q.dtype, dev)
@@ -217,7 +228,8 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
                             q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=_ptr(g),
                             beta=beta.data_ptr(), o=out.data_ptr(), gate=_gate_tuple(gate),
                             state_indices=_ptr(state_indices),
-                            n_slots=S if state_indices is not None else 0)
+                            n_slots=S if state_indices is not None else 0, n_k_heads=Hg,
+                            qk_l2norm=int(bool(qk_l2norm)))
     st = _abi.recurrent_decode_raw(desc, _stream(stream))
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_recurrent_decode")

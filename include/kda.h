@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -108,9 +108,15 @@ typedef enum { KDA_PLAN_AUTO = 0, KDA_PLAN_FUSED = 1, KDA_PLAN_TWO_PASS = 2 } kd
  * commit message) gives the same result as the token loop up to rounding, for
  * any chunk size.
  *
- * Layouts: q, k, g [T_total, H, dk]; v, o [T_total, H, dv]; beta [T_total, H];
- * h0, ht [N, H, dk, dv].  An empty sequence (length 0) writes no o and sets
- * ht = h0 (zeros when h0 is NULL).
+ * Layouts: q, k [T_total, Hg, dk]; g [T_total, H, dk]; v, o [T_total, H, dv];
+ * beta [T_total, H]; h0, ht [N, H, dk, dv].  Hg = n_k_heads key/query heads
+ * are shared by groups of H / Hg consecutive value heads: value head h reads
+ * key head h / (H / Hg) (Hg = H, the default, is one key head per head).  An
+ * empty sequence (length 0) writes no o and sets ht = h0 (zeros when h0 is
+ * NULL).
+ *
+ * qk_l2norm = 1 normalises every q and k row (one token, one key head) inside
+ * the kernels before use: q / sqrt(sum q^2 + 1e-6), in fp32.
  *
  * cu_seqlens: device int32 [N + 1], cu[0] = 0, non-decreasing,
  * cu[N] = t_total.  May be NULL only when n_seqs == 1.  Its contents are read
@@ -148,11 +154,14 @@ typedef struct {
                               /* the sequence: no o, no state.  Indices must   */
                               /* be distinct.                                  */
   int32_t n_slots;            /* pool size when state_indices is set           */
+  int32_t n_k_heads;          /* Hg, dividing H; 0 = H                         */
+  int32_t qk_l2norm;          /* 1 = L2-normalise q and k rows in the kernels  */
 } kda_prefill_desc;
 
 /* One recurrent decode step for a batch of N sequences, one token each.
- * state [N, H, dk, dv] fp32 is read and updated IN PLACE; q, k, g [N, H, dk];
- * v, o [N, H, dv]; beta [N, H].  o must not overlap state or any input. */
+ * state [N, H, dk, dv] fp32 is read and updated IN PLACE; q, k [N, Hg, dk];
+ * g [N, H, dk]; v, o [N, H, dv]; beta [N, H].  n_k_heads and qk_l2norm as in
+ * kda_prefill_desc.  o must not overlap state or any input. */
 typedef struct {
   uint32_t struct_size;       /* sizeof(kda_decode_desc)                        */
   int32_t dtype;              /* kda_dtype of q, k, v, beta, o                  */
@@ -173,6 +182,8 @@ typedef struct {
                               /* state_indices[n]; negative (or >= n_slots)    */
                               /* skips it (no o).  Indices must be distinct.   */
   int32_t n_slots;            /* pool size when state_indices is set           */
+  int32_t n_k_heads;          /* Hg, dividing H; 0 = H                         */
+  int32_t qk_l2norm;          /* 1 = L2-normalise q and k in the kernel        */
 } kda_decode_desc;
 
 /* Recurrent prefill: the same computation as kda_chunk_prefill (same

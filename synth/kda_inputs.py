@@ -5,7 +5,9 @@ adding a tensor never shifts the others):
 
   stream  tensor   distribution
   1       q        N(0, 1), then L2-normalised over dk per (token, head)
-  2       k        N(0, 1), then L2-normalised over dk per (token, head)
+                   (left raw when the kernels are to normalise it)
+  2       k        N(0, 1), likewise; q and k have n_k_heads heads (= H by
+                   default), v, g, beta and the state H
   3       v        N(0, 1)
   4       beta     sigmoid(N(0, 1))                                [T, H]
   5       gate x   N(0, 1)                                         [T, H, dk]
@@ -85,8 +87,8 @@ def _softplus(x: np.ndarray) -> np.ndarray:
 class KdaInputs:
     """One packed batch.  Storage arrays are what the GPU path receives."""
 
-    q: np.ndarray  # [T, H, dk]   f32 or bf16 bits
-    k: np.ndarray  # [T, H, dk]
+    q: np.ndarray  # [T, Hg, dk]  f32 or bf16 bits (Hg = H unless key heads are grouped)
+    k: np.ndarray  # [T, Hg, dk]
     v: np.ndarray  # [T, H, dv]
     g: np.ndarray  # [T, H, dk]   fp32 natural-log decay, <= 0
     beta: np.ndarray  # [T, H]
@@ -110,6 +112,10 @@ class KdaInputs:
 
     @property
     def H(self) -> int:
+        return int(self.v.shape[1])
+
+    @property
+    def Hg(self) -> int:
         return int(self.q.shape[1])
 
     @property
@@ -155,9 +161,17 @@ def make_inputs(
     h0_std: float = 0.0,
     chunk: int = 64,
     scale: Optional[float] = None,
+    n_k_heads: Optional[int] = None,
+    qk_prenorm: bool = True,
 ) -> KdaInputs:
-    """Packed varlen batch with the recipe in the module docstring."""
+    """Packed varlen batch with the recipe in the module docstring.
+    n_k_heads: q/k heads (a divisor of H; default H).  qk_prenorm = False
+    leaves q and k unnormalised (for kernels that normalise them)."""
     dv = dk if dv is None else dv
+    Hg = H if n_k_heads is None else int(n_k_heads)
+    if Hg < 1 or H % Hg:
+        raise ValueError(f"n_k_heads {Hg} must divide H = {H}")
+    qk = _l2norm if qk_prenorm else (lambda a: a)
     lengths = [int(x) for x in lengths]
     if any(x < 0 for x in lengths):
         raise ValueError("negative sequence length")
@@ -169,10 +183,10 @@ def make_inputs(
     # The independent streams are drawn on worker threads (numpy's generators
     # release the GIL); each stream's values do not depend on the threading.
     def draw_q():
-        return _store(_l2norm(_rng(seed, "q").standard_normal((T, H, dk))), dtype)
+        return _store(qk(_rng(seed, "q").standard_normal((T, Hg, dk))), dtype)
 
     def draw_k():
-        return _store(_l2norm(_rng(seed, "k").standard_normal((T, H, dk))), dtype)
+        return _store(qk(_rng(seed, "k").standard_normal((T, Hg, dk))), dtype)
 
     def draw_v():
         return _store(_rng(seed, "v").standard_normal((T, H, dv)), dtype)
@@ -212,7 +226,8 @@ def make_inputs(
         dtype=dtype,
         chunk=chunk,
         scale=float(dk ** -0.5) if scale is None else float(scale),
-        meta={"seed": seed, "lengths": lengths, "gate": gate, "h0_std": h0_std},
+        meta={"seed": seed, "lengths": lengths, "gate": gate, "h0_std": h0_std,
+              "qk_prenorm": qk_prenorm},
         gate_x=x_s,
         gate_a_log=a_s,
         gate_dt_bias=b_s,
@@ -261,6 +276,8 @@ def make_config(cfg_id: int, heads: Optional[Sequence[int]] = None) -> KdaInputs
 
 
 def slice_heads(inp: KdaInputs, heads: Sequence[int]) -> KdaInputs:
+    if inp.Hg != inp.H:
+        raise ValueError("slice_heads needs one key head per head")
     hs = np.asarray(list(heads), dtype=np.int64)
     return KdaInputs(
         q=np.ascontiguousarray(inp.q[:, hs]),

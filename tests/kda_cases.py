@@ -46,13 +46,23 @@ def dev_gate(inp: synth.KdaInputs, dev="cuda") -> tuple:
             to_dev(inp.gate_dt_bias, "f32", dev))
 
 
-def oracle_prefill(inp: synth.KdaInputs, fused_gate: bool = False):
+def oracle_qk(inp: synth.KdaInputs, f: dict, qk_l2norm: bool = False):
+    """q and k as the oracle consumes them: normalised when the kernels are
+    asked to normalise, and expanded from Hg key heads to the H heads."""
+    q, k = f["q"], f["k"]
+    if qk_l2norm:
+        q, k = oracle.l2norm(q), oracle.l2norm(k)
+    return oracle.expand_key_heads(q, inp.H), oracle.expand_key_heads(k, inp.H)
+
+
+def oracle_prefill(inp: synth.KdaInputs, fused_gate: bool = False, qk_l2norm: bool = False):
     """fp64 oracle on the rounded inputs; with fused_gate, g is recomputed by
-    the oracle from the stored raw gate (what the fused-gate path receives)."""
+    the oracle from the stored raw gate (what the fused-gate path receives);
+    with qk_l2norm, q and k are normalised by the oracle first."""
     f = inp.f64()
     g = oracle.kimi_gate(*inp.gate_f64()) if fused_gate else f["g"]
-    return oracle.prefill(f["q"], f["k"], f["v"], g, f["beta"], f["h0"], f["cu_seqlens"],
-                          f["scale"])
+    q, k = oracle_qk(inp, f, qk_l2norm)
+    return oracle.prefill(q, k, f["v"], g, f["beta"], f["h0"], f["cu_seqlens"], f["scale"])
 
 
 def say(msg: str):

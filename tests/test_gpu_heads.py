@@ -1,0 +1,130 @@
+"""GPU parity of the q/k options: in-kernel L2 normalisation of q and k
+(qk_l2norm) and grouped key heads (Hg key heads shared by H value heads),
+against the fp64 oracle (oracle/heads.py applied before the recurrence).
+Bars as everywhere: relative L2 <= 1e-4 (fp32) / 1e-2 (bf16) for o and the
+final state."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kda_cases import TOL, dev_gate, dev_inputs, oracle_prefill, oracle_qk, rel_l2, say, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_55_amd as m
+
+    return m
+
+
+def prefill(kda, inp, norm, fused_gate=False, recurrent=False):
+    d = dev_inputs(inp)
+    gate = dev_gate(inp) if fused_gate else None
+    g = None if fused_gate else d["g"]
+    if recurrent:
+        o, ht = kda.recurrent_prefill(d["q"], d["k"], d["v"], g, d["beta"], d["h0"],
+                                      d["cu_seqlens"], scale=inp.scale, gate=gate, qk_l2norm=norm)
+    else:
+        o, ht = kda.chunk_prefill(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], d["cu_seqlens"],
+                                  scale=inp.scale, chunk=inp.chunk, gate=gate, qk_l2norm=norm)
+    torch.cuda.synchronize()
+    return to_host64(o), to_host64(ht)
+
+
+CASES = [
+    # dtype, d, chunk, lengths, H, Hg, norm, gate
+    ("f32", 32, 16, [70], 4, 2, False, "softplus"),
+    ("f32", 64, 32, [45, 0, 80], 4, 1, True, "softplus"),
+    ("f32", 128, 16, [33], 2, 2, True, "softplus"),
+    ("bf16", 128, 64, [300], 4, 2, True, "kimi"),
+    ("bf16", 128, 64, [64, 1, 129], 6, 3, False, "kimi"),
+    ("bf16", 64, 16, [90, 17], 4, 4, True, "kimi"),
+    ("bf16", 128, 32, [150], 8, 1, True, "kimi"),
+    ("bf16", 32, 64, [200, 3], 4, 2, True, "kimi"),
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,lengths,H,Hg,norm,gate", CASES)
+def test_chunk_prefill(kda, dtype, d, chunk, lengths, H, Hg, norm, gate):
+    say(f"chunk prefill dtype={dtype} d={d} C={chunk} lengths={lengths} H={H} Hg={Hg} norm={norm}")
+    inp = synth.make_inputs(51, lengths, H, d, dtype=dtype, gate=gate, h0_std=0.05, chunk=chunk,
+                            n_k_heads=Hg, qk_prenorm=not norm)
+    o, ht = prefill(kda, inp, norm)
+    o_ref, ht_ref = oracle_prefill(inp, qk_l2norm=norm)
+    eo, es = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,lengths,H,Hg", [("f32", 64, [20, 0, 33], 4, 2),
+                                                   ("bf16", 128, [17, 40], 4, 1)])
+def test_recurrent_prefill_and_fused_gate(kda, dtype, d, lengths, H, Hg):
+    say(f"recurrent prefill + fused gate dtype={dtype} d={d} H={H} Hg={Hg} norm")
+    inp = synth.make_inputs(52, lengths, H, d, dtype=dtype, gate="kimi", h0_std=0.05,
+                            n_k_heads=Hg, qk_prenorm=False)
+    o, ht = prefill(kda, inp, True, fused_gate=True, recurrent=True)
+    o_ref, ht_ref = oracle_prefill(inp, fused_gate=True, qk_l2norm=True)
+    eo, es = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    oc, hc = prefill(kda, inp, True, fused_gate=True)
+    say(f"  chunked: rel-L2 o={rel_l2(oc, o_ref):.3e} state={rel_l2(hc, ht_ref):.3e}")
+    assert rel_l2(oc, o_ref) <= TOL[dtype] and rel_l2(hc, ht_ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,d,H,Hg,norm", [("f32", 32, 4, 2, True), ("f32", 128, 4, 1, False),
+                                               ("bf16", 128, 8, 2, True), ("bf16", 64, 4, 4, True)])
+def test_decode(kda, dtype, d, H, Hg, norm):
+    say(f"decode dtype={dtype} d={d} H={H} Hg={Hg} norm={norm}")
+    N = 5
+    inp = synth.make_inputs(53, [1] * N, H, d, dtype=dtype, h0_std=0.5, n_k_heads=Hg,
+                            qk_prenorm=not norm)
+    dev = dev_inputs(inp)
+    state = dev["h0"].clone()
+    o = kda.recurrent_decode(state, dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                             scale=inp.scale, qk_l2norm=norm)
+    # the recurrent prefill over one token per sequence is the same arithmetic
+    o2, st2 = kda.recurrent_prefill(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"],
+                                    dev["h0"], dev["cu_seqlens"], scale=inp.scale,
+                                    qk_l2norm=norm)
+    torch.cuda.synchronize()
+    f = inp.f64()
+    q, k = oracle_qk(inp, f, norm)
+    o_ref, st_ref = oracle.decode(f["h0"], q, k, f["v"], f["g"], f["beta"], f["scale"])
+    eo, es = rel_l2(to_host64(o), o_ref), rel_l2(to_host64(state), st_ref)
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL[dtype] and es <= 1e-5
+    assert torch.equal(o, o2) and torch.equal(state, st2)
+
+
+def test_norm_of_unit_rows_is_nearly_identity(kda):
+    """On rows already of unit norm the in-kernel normalisation changes q and
+    k by a factor 1 / sqrt(1 + 1e-6) at most: fp32 results agree to 1e-5."""
+    say("in-kernel norm on prenormalised fp32 inputs")
+    inp = synth.make_inputs(54, [100, 37], 3, 64, dtype="f32", gate="softplus", h0_std=0.05,
+                            chunk=32)
+    o1, s1 = prefill(kda, inp, False)
+    o2, s2 = prefill(kda, inp, True)
+    say(f"  rel diff o={rel_l2(o2, o1):.3e} state={rel_l2(s2, s1):.3e}")
+    assert rel_l2(o2, o1) <= 1e-5 and rel_l2(s2, s1) <= 1e-5
+
+
+@pytest.mark.parametrize("Hg", [32, 8])
+def test_prefill_4k_raw_qk(kda, Hg):
+    """The 4096-token workload shape (H = 32, d = 128, chunk 64, bf16, Kimi
+    gate) with raw q and k normalised in the kernels, all heads against the
+    oracle; Hg = 8 groups four value heads per key head."""
+    say(f"prefill 4k, raw q/k, in-kernel norm, Hg={Hg}")
+    inp = synth.make_inputs(55, [4096], 32, 128, dtype="bf16", gate="kimi", h0_std=0.02,
+                            n_k_heads=Hg, qk_prenorm=False)
+    o, ht = prefill(kda, inp, True)
+    o_ref, ht_ref = oracle_prefill(inp, qk_l2norm=True)
+    eo, es = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
