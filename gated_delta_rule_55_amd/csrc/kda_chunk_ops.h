@@ -747,21 +747,33 @@ struct ChunkLocal {
 };
 
 // ---------------------------------------------------------------------------
-// One step of the state scan for 16 value columns (block jb), split over the
-// workgroup's KBD waves by dk slice: wave w owns state rows 32w .. 32w + 31
-// (accumulator tiles, rows 32w + 16m + 4lg + j, column 16jb + l16).
-template <typename TIO, int D, int C>
+// One step of the state scan for NJ tiles of 16 value columns (block jb =
+// columns 16 NJ jb .. 16 NJ jb + 16 NJ - 1), split over the workgroup's KBD
+// waves by dk slice: wave w owns state rows 32w .. 32w + 31 of every tile
+// (accumulator tiles S[c][m], rows 32w + 16m + 4lg + j, column
+// 16 (NJ jb + c) + l16).  The NJ column tiles share one load of the chunk's
+// W, Q' and Kg, so a wider block reads those operators fewer times in total.
+template <typename TIO, int D, int C, int NJ = 1>
 struct ScanStep {
   using Gm = Geo<TIO, D, C>;
   using FragT = typename Frag<TIO>::type;
   static constexpr int TT = Gm::TT, DT = Gm::DT, KBD = Gm::KBD, KBC = Gm::KBC;
   static constexpr int VT_LD = Gm::VT_LD;
   static constexpr int NOWN = (TT + KBD - 1) / KBD;  // token tiles a wave reduces
+  static_assert(DT % NJ == 0, "column tiles per block must divide the head dim");
+  static constexpr int NB = DT / NJ;                  // column blocks per head
+  // LDS: v and o partials [2][NJ][KBD][TT][64] f32x4, V^T [NJ][16][VT_LD],
+  // o staging [C][OS_LD]
+  static constexpr size_t RED = (size_t)NJ * Gm::SCAN_RED;
+  static constexpr size_t OFF_VT = 2 * RED;
+  static constexpr int OS_LD = 16 * NJ + Gm::TP;
+  static constexpr size_t OFF_OS = align_up(OFF_VT + (size_t)NJ * 16 * VT_LD * sizeof(TIO), 16);
+  static constexpr size_t LDS_BYTES = OFF_OS + (size_t)C * OS_LD * sizeof(TIO);
 
   // Everything one step reads from a chunk's outputs, for this lane.
   struct Ops {
     FragT w[TT], q[TT], k[2][KBC];
-    TIO u[NOWN][4], ol[NOWN][4];
+    TIO u[NJ][NOWN][4], ol[NJ][NOWN][4];
     f32x4 gam[2];
     int start, len;  // the chunk's token range (set by the caller)
   };
@@ -787,17 +799,20 @@ struct ScanStep {
     const int w = threadIdx.x >> 6;
     if (!ALL && w >= KBD) return;
 #pragma unroll
-    for (int i = 0; i < NOWN; ++i) {
-      const int t0 = w + KBD * i;
-      const int t = t0 < TT ? t0 : TT - 1;  // tiles past the chunk are loaded, then unused
-      const TIO* Uc = in.u + ((size_t)(t * DT + jb) * 64 + lane) * 4;
-      const TIO* Oc = in.o + ((size_t)(t * DT + jb) * 64 + lane) * 4;
+    for (int c = 0; c < NJ; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        op.u[i][j] = Uc[j];
-        op.ol[i][j] = Oc[j];
+      for (int i = 0; i < NOWN; ++i) {
+        const int t0 = w + KBD * i;
+        const int t = t0 < TT ? t0 : TT - 1;  // tiles past the chunk are loaded, then unused
+        const int ct = NJ * jb + c;
+        const TIO* Uc = in.u + ((size_t)(t * DT + ct) * 64 + lane) * 4;
+        const TIO* Oc = in.o + ((size_t)(t * DT + ct) * 64 + lane) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          op.u[c][i][j] = Uc[j];
+          op.ol[c][i][j] = Oc[j];
+        }
       }
-    }
   }
   template <bool ALL>
   static __device__ __forceinline__ void load_kg(Ops& op, const ChunkOut<TIO>& in) {
@@ -822,71 +837,82 @@ struct ScanStep {
   }
 
   // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
-  // S = diag(Gam) S + Kg^T V.  Two workgroup barriers.  ALL: every wave of the
-  // workgroup holds a dk slice (no idle waves), which keeps the step free of
-  // divergent branches so the compiler can count outstanding loads exactly.
-  // NTH: threads of the workgroup.  With `nxt` set, each group of `op` is
-  // reloaded from *nxt as soon as the step has consumed it (the loads then
-  // overlap the rest of the step); nxt_ent supplies the new token range.
-  // live = false (uniform) runs the step without effect: no o rows are
-  // written and S keeps its value; the refills still happen.
+  // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Two workgroup
+  // barriers.  ALL: every wave of the workgroup holds a dk slice (no idle
+  // waves), which keeps the step free of divergent branches so the compiler
+  // can count outstanding loads exactly.  NTH: threads of the workgroup.
+  // With `nxt` set, each group of `op` is reloaded from *nxt as soon as the
+  // step has consumed it (the loads then overlap the rest of the step);
+  // nxt_ent supplies the new token range.  live = false (uniform) runs the
+  // step without effect: no o rows are written and S keeps its value; the
+  // refills still happen.
   template <bool ALL, int NTH>
-  static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[2], Ops& op,
+  static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[NJ][2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
                                               int jb, const ChunkOut<TIO>* nxt = nullptr,
                                               const ChunkEnt* nxt_ent = nullptr,
                                               bool live = true) {
     const int start = __builtin_amdgcn_readfirstlane(op.start);
     const int len = live ? __builtin_amdgcn_readfirstlane(op.len) : 0;
-    const f32x4 s_keep[2] = {S[0], S[1]};
-    f32x4* red_v = reinterpret_cast<f32x4*>(lds);                    // [KBD][TT][64]
-    f32x4* red_o = reinterpret_cast<f32x4*>(lds + Gm::SCAN_RED);      // [KBD][TT][64]
-    TIO* Vt = reinterpret_cast<TIO*>(lds + 2 * Gm::SCAN_RED);         // [16][VT_LD]
-    TIO* Os = reinterpret_cast<TIO*>(lds + Gm::OFF_OS);               // [C][OS_LD]
+    f32x4 s_keep[NJ][2];
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) {
+      s_keep[c][0] = S[c][0];
+      s_keep[c][1] = S[c][1];
+    }
+    f32x4* red_v = reinterpret_cast<f32x4*>(lds);          // [NJ][KBD][TT][64]
+    f32x4* red_o = reinterpret_cast<f32x4*>(lds + RED);    // [NJ][KBD][TT][64]
+    TIO* Vt = reinterpret_cast<TIO*>(lds + OFF_VT);        // [NJ][16][VT_LD]
+    TIO* Os = reinterpret_cast<TIO*>(lds + OFF_OS);        // [C][OS_LD]
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     const bool active = ALL || w < KBD;
 
     if (active) {
-      const FragT sb = frag_from_d<TIO>(S[0], S[1]);
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        red_v[(w * TT + t) * 64 + lane] = mma32(op.w[t], sb, zero4());
-        red_o[(w * TT + t) * 64 + lane] = mma32(op.q[t], sb, zero4());
+      for (int c = 0; c < NJ; ++c) {
+        const FragT sb = frag_from_d<TIO>(S[c][0], S[c][1]);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          red_v[((c * KBD + w) * TT + t) * 64 + lane] = mma32(op.w[t], sb, zero4());
+          red_o[((c * KBD + w) * TT + t) * 64 + lane] = mma32(op.q[t], sb, zero4());
+        }
       }
     }
     if (nxt) load_wq<ALL>(op, *nxt);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NOWN; ++i) {
-      const int t = w + KBD * i;
-      if (active && (TT % KBD == 0 || t < TT)) {
-        f32x4 vv, oo;
+    for (int c = 0; c < NJ; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vv[j] = to_f32(op.u[i][j]);
-          oo[j] = to_f32(op.ol[i][j]);
-        }
+      for (int i = 0; i < NOWN; ++i) {
+        const int t = w + KBD * i;
+        if (active && (TT % KBD == 0 || t < TT)) {
+          f32x4 vv, oo;
 #pragma unroll
-        for (int ww = 0; ww < KBD; ++ww) {
-          vv -= red_v[(ww * TT + t) * 64 + lane];
-          oo += red_o[(ww * TT + t) * 64 + lane];
-        }
+          for (int j = 0; j < 4; ++j) {
+            vv[j] = to_f32(op.u[c][i][j]);
+            oo[j] = to_f32(op.ol[c][i][j]);
+          }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 16 * t + 4 * lg + j;
-          Vt[l16 * VT_LD + r] = from_f32<TIO>(vv[j]);
-          Os[r * Gm::OS_LD + l16] = from_f32<TIO>(oo[j]);
+          for (int ww = 0; ww < KBD; ++ww) {
+            vv -= red_v[((c * KBD + ww) * TT + t) * 64 + lane];
+            oo += red_o[((c * KBD + ww) * TT + t) * 64 + lane];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 16 * t + 4 * lg + j;
+            Vt[(c * 16 + l16) * VT_LD + r] = from_f32<TIO>(vv[j]);
+            Os[r * OS_LD + 16 * c + l16] = from_f32<TIO>(oo[j]);
+          }
         }
       }
-    }
     if (nxt) load_uo<ALL>(op, *nxt, jb);
     __syncthreads();
     {
       // the chunk's rows of o as one raw buffer: rows >= len fall outside it;
       // 16-byte pieces, EPV values of one row each
-      constexpr int EPV = 16 / (int)sizeof(TIO), VPRO = 16 / EPV, NVEC = C * VPRO;
+      constexpr int EPV = 16 / (int)sizeof(TIO), VPRO = 16 * NJ / EPV, NVEC = C * VPRO;
       const __amdgpu_buffer_rsrc_t orsrc =
           make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
 #pragma unroll
@@ -894,28 +920,32 @@ struct ScanStep {
         const int x0 = (int)threadIdx.x + NTH * p;
         const int x = x0 < NVEC ? x0 : NVEC - 1;
         const int r = x / VPRO, cv = x % VPRO;
-        const uint4 val = *reinterpret_cast<const uint4*>(Os + r * Gm::OS_LD + cv * EPV);
+        const uint4 val = *reinterpret_cast<const uint4*>(Os + r * OS_LD + cv * EPV);
         const int off = (x0 < NVEC && r < len)
-                            ? (r * (int)ostride + h * D + 16 * jb + cv * EPV) * (int)sizeof(TIO)
+                            ? (r * (int)ostride + h * D + 16 * NJ * jb + cv * EPV) * (int)sizeof(TIO)
                             : kBufferOff;
         buffer_store16(val, orsrc, off);
       }
     }
     if (active) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        S[m] *= op.gam[m];
+      for (int c = 0; c < NJ; ++c)
 #pragma unroll
-        for (int kc = 0; kc < KBC; ++kc) {
-          // Kg fragments are in kperm token order; read V the same way
-          const FragT fv = load_frag_perm<TIO>(Vt + l16 * VT_LD + 32 * kc, lg);
-          S[m] = mma32(op.k[m][kc], fv, S[m]);
+        for (int m = 0; m < 2; ++m) {
+          S[c][m] *= op.gam[m];
+#pragma unroll
+          for (int kc = 0; kc < KBC; ++kc) {
+            // Kg fragments are in kperm token order; read V the same way
+            const FragT fv = load_frag_perm<TIO>(Vt + (c * 16 + l16) * VT_LD + 32 * kc, lg);
+            S[c][m] = mma32(op.k[m][kc], fv, S[c][m]);
+          }
         }
-      }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int c = 0; c < NJ; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) S[m][j] = live ? S[m][j] : s_keep[m][j];
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) S[c][m][j] = live ? S[c][m][j] : s_keep[c][m][j];
     }
     if (nxt) {
       load_kg<ALL>(op, *nxt);
@@ -926,8 +956,8 @@ struct ScanStep {
 
   // Token slots past the chunk's tiles (C < 32) must read as zero.
   static __device__ __forceinline__ void clear_vt(unsigned char* lds) {
-    TIO* Vt = reinterpret_cast<TIO*>(lds + 2 * Gm::SCAN_RED);
-    for (int x = threadIdx.x; x < 16 * VT_LD; x += blockDim.x) Vt[x] = from_f32<TIO>(0.f);
+    TIO* Vt = reinterpret_cast<TIO*>(lds + OFF_VT);
+    for (int x = threadIdx.x; x < NJ * 16 * VT_LD; x += blockDim.x) Vt[x] = from_f32<TIO>(0.f);
   }
 };
 

@@ -193,17 +193,42 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
 }
 
 // Two-pass plan, stage 2: state scan with the output, one workgroup of D/32
-// waves per (sequence, head, 16 value columns), the next chunk's operators
-// loaded while the current one computes.
-template <typename TIO, int D, int C>
+// waves per (sequence, head, block of 16 NJ value columns), the next chunks'
+// operators loaded while the current one computes.  The column blocks of a
+// head all read the chunk's W, Q' and Kg, so wider blocks (NJ tiles of 16
+// columns) cut that shared traffic through L2 at the price of fewer, busier
+// workgroups.
+//
+// Which width is faster depends on the batch.  A step's latency grows with
+// the width (more MFMA and LDS work per workgroup between barriers), while the
+// L2 traffic for the shared operators shrinks with it; measured on MI355X at
+// H = 32, d = 128, C = 64 (ms of the scan stage):
+//     one 32k sequence:   NJ 1: 0.62   NJ 2: 0.83   NJ 4: 1.42
+//     four 32k sequences: NJ 1: 2.44   NJ 2: 1.67   NJ 4: 1.56
+// A single sequence is bound by its chain of steps, a batch by the shared
+// traffic.  The launch takes the widest block that still leaves every CU at
+// least one workgroup (bf16 only: the fp32 fragments are twice the registers).
+template <typename TIO, int D, int NJ>
+constexpr int kScanTilesMax = (sizeof(TIO) == 2 && (D / 16) % NJ == 0) ? NJ : 1;
+
+template <typename TIO, int D>
+int scan_tiles(int n_seqs, int n_heads, int cus) {
+  const int64_t heads = (int64_t)n_seqs * n_heads;
+  for (int nj : {4, 2}) {
+    if (sizeof(TIO) != 2 || (D / 16) % nj != 0) continue;
+    if (heads * (D / 16 / nj) >= cus) return nj;
+  }
+  return 1;
+}
+template <typename TIO, int D, int C, int NJ>
 __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     const float* __restrict__ h0, float* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
     int n_heads, const int* __restrict__ status, const int* __restrict__ chunk_off,
     const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks,
     const int* __restrict__ slots, int n_slots) {
   using Gm = Geo<TIO, D, C>;
-  using SS = ScanStep<TIO, D, C>;
-  constexpr int NB = D / 16;
+  using SS = ScanStep<TIO, D, C, NJ>;
+  constexpr int NB = SS::NB;  // column blocks of 16 NJ columns per head
   extern __shared__ __align__(16) unsigned char lds[];
   if (*status != 0) return;
 
@@ -226,25 +251,29 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     if (slot < 0 || slot >= n_slots) return;
   }
   SS::clear_vt(lds);
-  f32x4 S[2];
+  f32x4 S[NJ][2];
   const size_t sbase = ((size_t)slot * n_heads + h) * D * D;
+  // no h0: an empty buffer, whose loads read 0 (branch-free, so the compiler
+  // keeps exact counts of the loads in flight)
+  const __amdgpu_buffer_rsrc_t hr =
+      make_rsrc(const_cast<float*>(h0 ? h0 + sbase : h0), h0 ? D * D * 4 : 0);
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int c = 0; c < NJ; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // no h0: an empty buffer, whose loads read 0 (branch-free, so the
-      // compiler keeps exact counts of the loads in flight)
-      const __amdgpu_buffer_rsrc_t hr =
-          make_rsrc(const_cast<float*>(h0 ? h0 + sbase : h0), h0 ? D * D * 4 : 0);
-      S[m][j] = buffer_load_f32(hr, ((32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16) * 4);
-    }
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        S[c][m][j] = buffer_load_f32(
+            hr, ((32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16) * 4);
   // Take delivery of h0 here, before the operator loads are issued: S then
   // enters the loop with nothing in flight, and the loop's own waits are
   // counted exactly (an empty asm that reads and writes S; emits nothing).
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int c = 0; c < NJ; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(S[m][j]));
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(S[c][m][j]));
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const int64_t ostride = (int64_t)n_heads * D;
@@ -288,10 +317,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   }
   if (ht) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int c = 0; c < NJ; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ht[sbase + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16] = S[m][j];
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          ht[sbase + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16] =
+              S[c][m][j];
   }
 }
 
@@ -445,14 +477,14 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
   // ---- consumer: every chunk, this member's 16 columns ----------------------
   Cursor cc;
   cursor_task(cc, 0, team, a);
-  f32x4 S[2];
+  f32x4 S[1][2];
   auto state_in = [&]() {
     const size_t sb = ((size_t)cc.n * a.n_heads + cc.h) * D * D;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        S[m][j] = (a.h0 && w < Gm::KBD)
+        S[0][m][j] = (a.h0 && w < Gm::KBD)
                       ? a.h0[sb + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16]
                       : 0.f;
   };
@@ -463,7 +495,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        a.ht[sb + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16] = S[m][j];
+        a.ht[sb + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16] = S[0][m][j];
   };
   // Enter the task under cc; empty tasks pass h0 through to ht.
   auto enter_tasks = [&]() {
@@ -514,6 +546,22 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
       __hip_atomic_fetch_add(done + (s0 + tid) % R, 1, __ATOMIC_RELEASE,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <typename TIO, int D, int C, int NJ>
+hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk_off,
+                       const ChunkEnt* tab, unsigned char* blocks, hipStream_t stream) {
+  using SS = ScanStep<TIO, D, C, NJ>;
+  static_assert(SS::LDS_BYTES <= 160 * 1024, "scan LDS");
+  hipError_t err = hipFuncSetAttribute((const void*)state_scan_kernel<TIO, D, C, NJ>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)SS::LDS_BYTES);
+  if (err != hipSuccess) return err;
+  const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * SS::NB);
+  hipLaunchKernelGGL((state_scan_kernel<TIO, D, C, NJ>), dim3(nblk), dim3(64 * (D / 32)),
+                     SS::LDS_BYTES, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
+                     chunk_off, tab, blocks, a.slots, a.n_slots);
+  return hipGetLastError();
 }
 
 template <typename TIO, int D, int C>
@@ -628,11 +676,12 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
                          QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
-    const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * (D / 16));
-    hipLaunchKernelGGL((state_scan_kernel<TIO, D, C>), dim3(nblk), dim3(64 * (D / 32)),
-                       Gm::SCAN_LDS, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
-                       chunk_off, tab, blocks, a.slots, a.n_slots);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    switch (scan_tiles<TIO, D>(a.n_seqs, a.n_heads, cus)) {
+      case 4: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 4>>(a, status, chunk_off, tab, blocks, stream); break;
+      case 2: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 2>>(a, status, chunk_off, tab, blocks, stream); break;
+      default: err = launch_scan<TIO, D, C, 1>(a, status, chunk_off, tab, blocks, stream); break;
+    }
+    if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
     return hipSuccess;
   }

@@ -159,7 +159,14 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    handles = None if events is None else [e.cuda_event for e in events]
+    handles = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events must be four torch.cuda.Event objects")
+        for e in events:  # torch creates the HIP event on its first record
+            if e.cuda_event == 0:
+                e.record(torch.cuda.current_stream() if stream is None else stream)
+        handles = [e.cuda_event for e in events]
     st = _abi.chunk_prefill_timed_raw(desc, workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(),
                                       _stream(stream), handles)
