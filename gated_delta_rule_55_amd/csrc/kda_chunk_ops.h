@@ -748,35 +748,46 @@ struct ChunkLocal {
 
 // ---------------------------------------------------------------------------
 // One step of the state scan for NJ tiles of 16 value columns (block jb =
-// columns 16 NJ jb .. 16 NJ jb + 16 NJ - 1), split over the workgroup's KBD
-// waves by dk slice: wave w owns state rows 32w .. 32w + 31 of every tile
-// (accumulator tiles S[c][m], rows 32w + 16m + 4lg + j, column
-// 16 (NJ jb + c) + l16).  The NJ column tiles share one load of the chunk's
-// W, Q' and Kg, so a wider block reads those operators fewer times in total.
+// columns 16 NJ jb .. 16 NJ jb + 16 NJ - 1) by the workgroup's KBD waves.
+// Wave w owns
+//   - dk slice w of the state: rows 32w .. 32w + 31 of every column tile
+//     (accumulator tiles S[c][m], rows 32w + 16m + 4lg + j, column
+//     16 (NJ jb + c) + l16), which it updates with Kg^T V;
+//   - token tiles t = w + KBD i of the chunk, for which it computes the whole
+//     products W S and Q' S over all of dk, so no partial sums cross waves.
+// The waves exchange only the state slices (as bf16 B fragments, 1 KB per
+// slice and column tile) and V (16 tokens x 16 columns per tile).  The NJ
+// column tiles share one load of the chunk's W, Q' and Kg, so a wider block
+// reads those operators fewer times in total.
 template <typename TIO, int D, int C, int NJ = 1>
 struct ScanStep {
   using Gm = Geo<TIO, D, C>;
   using FragT = typename Frag<TIO>::type;
   static constexpr int TT = Gm::TT, DT = Gm::DT, KBD = Gm::KBD, KBC = Gm::KBC;
   static constexpr int VT_LD = Gm::VT_LD;
-  static constexpr int NOWN = (TT + KBD - 1) / KBD;  // token tiles a wave reduces
+  static constexpr int NOWN = (TT + KBD - 1) / KBD;  // token tiles a wave owns
   static_assert(DT % NJ == 0, "column tiles per block must divide the head dim");
   static constexpr int NB = DT / NJ;                  // column blocks per head
-  // LDS: v and o partials [2][NJ][KBD][TT][64] f32x4, V^T [NJ][16][VT_LD],
+  // LDS: state slices [NJ][KBD][64] fragments, V^T [NJ][16][VT_LD],
   // o staging [C][OS_LD]
-  static constexpr size_t RED = (size_t)NJ * Gm::SCAN_RED;
-  static constexpr size_t OFF_VT = 2 * RED;
+  static constexpr size_t SX_BYTES = (size_t)NJ * KBD * 64 * sizeof(FragT);
+  static constexpr size_t OFF_VT = SX_BYTES;
   static constexpr int OS_LD = 16 * NJ + Gm::TP;
   static constexpr size_t OFF_OS = align_up(OFF_VT + (size_t)NJ * 16 * VT_LD * sizeof(TIO), 16);
   static constexpr size_t LDS_BYTES = OFF_OS + (size_t)C * OS_LD * sizeof(TIO);
 
   // Everything one step reads from a chunk's outputs, for this lane.
   struct Ops {
-    FragT w[TT], q[TT], k[2][KBC];
+    FragT w[NOWN][KBD], q[NOWN][KBD], k[2][KBC];
     TIO u[NJ][NOWN][4], ol[NJ][NOWN][4];
     f32x4 gam[2];
     int start, len;  // the chunk's token range (set by the caller)
   };
+
+  static __device__ __forceinline__ int own_tile(int w, int i) {
+    const int t = w + KBD * i;
+    return t < TT ? t : TT - 1;  // tiles past the chunk are loaded, then unused
+  }
 
   // Loads of one chunk's operators, in three groups that a step consumes in
   // turn (W and Q', then U and Ol, then Kg and Gam), so a step can refill each
@@ -788,10 +799,13 @@ struct ScanStep {
     const int w = threadIdx.x >> 6;
     if (!ALL && w >= KBD) return;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      op.w[t] = load_frag8<TIO>(in.w + ((size_t)(t * KBD + w) * 64 + lane) * 8);
-      op.q[t] = load_frag8<TIO>(in.q + ((size_t)(t * KBD + w) * 64 + lane) * 8);
-    }
+    for (int i = 0; i < NOWN; ++i)
+#pragma unroll
+      for (int s = 0; s < KBD; ++s) {
+        const size_t f = ((size_t)(own_tile(w, i) * KBD + s) * 64 + lane) * 8;
+        op.w[i][s] = load_frag8<TIO>(in.w + f);
+        op.q[i][s] = load_frag8<TIO>(in.q + f);
+      }
   }
   template <bool ALL>
   static __device__ __forceinline__ void load_uo(Ops& op, const ChunkOut<TIO>& in, int jb) {
@@ -802,8 +816,7 @@ struct ScanStep {
     for (int c = 0; c < NJ; ++c)
 #pragma unroll
       for (int i = 0; i < NOWN; ++i) {
-        const int t0 = w + KBD * i;
-        const int t = t0 < TT ? t0 : TT - 1;  // tiles past the chunk are loaded, then unused
+        const int t = own_tile(w, i);
         const int ct = NJ * jb + c;
         const TIO* Uc = in.u + ((size_t)(t * DT + ct) * 64 + lane) * 4;
         const TIO* Oc = in.o + ((size_t)(t * DT + ct) * 64 + lane) * 4;
@@ -836,16 +849,29 @@ struct ScanStep {
     load_kg<ALL>(op, in);
   }
 
+  // Publish this wave's state slices as B fragments for the next step (every
+  // wave of the workgroup calls it; a barrier must follow before they are read).
+  static __device__ __forceinline__ void publish(unsigned char* lds, const f32x4 (&S)[NJ][2],
+                                                 bool active) {
+    FragT* Sx = reinterpret_cast<FragT*>(lds);
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    if (!active) return;
+#pragma unroll
+    for (int c = 0; c < NJ; ++c) Sx[(c * KBD + w) * 64 + lane] = frag_from_d<TIO>(S[c][0], S[c][1]);
+  }
+
   // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
-  // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Two workgroup
-  // barriers.  ALL: every wave of the workgroup holds a dk slice (no idle
-  // waves), which keeps the step free of divergent branches so the compiler
-  // can count outstanding loads exactly.  NTH: threads of the workgroup.
-  // With `nxt` set, each group of `op` is reloaded from *nxt as soon as the
-  // step has consumed it (the loads then overlap the rest of the step);
-  // nxt_ent supplies the new token range.  live = false (uniform) runs the
-  // step without effect: no o rows are written and S keeps its value; the
-  // refills still happen.
+  // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Expects the
+  // state slices published (publish(), then a barrier) and leaves them
+  // published for the next step.  Two workgroup barriers.  ALL: every wave
+  // of the workgroup holds a dk slice (no idle waves), which keeps the step
+  // free of divergent branches so the compiler can count outstanding loads
+  // exactly.  NTH: threads of the workgroup.  With `nxt` set, each group of
+  // `op` is reloaded from *nxt as soon as the step has consumed it (the loads
+  // then overlap the rest of the step); nxt_ent supplies the new token range.
+  // live = false (uniform) runs the step without effect: no o rows are
+  // written and S keeps its value; the refills still happen.
   template <bool ALL, int NTH>
   static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[NJ][2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
@@ -854,14 +880,7 @@ struct ScanStep {
                                               bool live = true) {
     const int start = __builtin_amdgcn_readfirstlane(op.start);
     const int len = live ? __builtin_amdgcn_readfirstlane(op.len) : 0;
-    f32x4 s_keep[NJ][2];
-#pragma unroll
-    for (int c = 0; c < NJ; ++c) {
-      s_keep[c][0] = S[c][0];
-      s_keep[c][1] = S[c][1];
-    }
-    f32x4* red_v = reinterpret_cast<f32x4*>(lds);          // [NJ][KBD][TT][64]
-    f32x4* red_o = reinterpret_cast<f32x4*>(lds + RED);    // [NJ][KBD][TT][64]
+    const FragT* Sx = reinterpret_cast<const FragT*>(lds);  // [NJ][KBD][64]
     TIO* Vt = reinterpret_cast<TIO*>(lds + OFF_VT);        // [NJ][16][VT_LD]
     TIO* Os = reinterpret_cast<TIO*>(lds + OFF_OS);        // [C][OS_LD]
     const int lane = threadIdx.x & 63;
@@ -872,42 +891,33 @@ struct ScanStep {
     if (active) {
 #pragma unroll
       for (int c = 0; c < NJ; ++c) {
-        const FragT sb = frag_from_d<TIO>(S[c][0], S[c][1]);
+        FragT sb[KBD];
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          red_v[((c * KBD + w) * TT + t) * 64 + lane] = mma32(op.w[t], sb, zero4());
-          red_o[((c * KBD + w) * TT + t) * 64 + lane] = mma32(op.q[t], sb, zero4());
+        for (int s2 = 0; s2 < KBD; ++s2) sb[s2] = Sx[(c * KBD + s2) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < NOWN; ++i) {
+          const int t = w + KBD * i;
+          if (TT % KBD == 0 || t < TT) {
+            f32x4 pv = zero4(), po = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < KBD; ++s2) {
+              pv = mma32(op.w[i][s2], sb[s2], pv);
+              po = mma32(op.q[i][s2], sb[s2], po);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 16 * t + 4 * lg + j;
+              Vt[(c * 16 + l16) * VT_LD + r] = from_f32<TIO>(to_f32(op.u[c][i][j]) - pv[j]);
+              Os[r * OS_LD + 16 * c + l16] = from_f32<TIO>(to_f32(op.ol[c][i][j]) + po[j]);
+            }
+          }
         }
       }
     }
-    if (nxt) load_wq<ALL>(op, *nxt);
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NJ; ++c)
-#pragma unroll
-      for (int i = 0; i < NOWN; ++i) {
-        const int t = w + KBD * i;
-        if (active && (TT % KBD == 0 || t < TT)) {
-          f32x4 vv, oo;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vv[j] = to_f32(op.u[c][i][j]);
-            oo[j] = to_f32(op.ol[c][i][j]);
-          }
-#pragma unroll
-          for (int ww = 0; ww < KBD; ++ww) {
-            vv -= red_v[((c * KBD + ww) * TT + t) * 64 + lane];
-            oo += red_o[((c * KBD + ww) * TT + t) * 64 + lane];
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 16 * t + 4 * lg + j;
-            Vt[(c * 16 + l16) * VT_LD + r] = from_f32<TIO>(vv[j]);
-            Os[r * OS_LD + 16 * c + l16] = from_f32<TIO>(oo[j]);
-          }
-        }
-      }
-    if (nxt) load_uo<ALL>(op, *nxt, jb);
+    if (nxt) {
+      load_wq<ALL>(op, *nxt);
+      load_uo<ALL>(op, *nxt, jb);
+    }
     __syncthreads();
     {
       // the chunk's rows of o as one raw buffer: rows >= len fall outside it;
@@ -932,26 +942,24 @@ struct ScanStep {
       for (int c = 0; c < NJ; ++c)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          S[c][m] *= op.gam[m];
+          f32x4 sn = S[c][m] * op.gam[m];
 #pragma unroll
           for (int kc = 0; kc < KBC; ++kc) {
             // Kg fragments are in kperm token order; read V the same way
             const FragT fv = load_frag_perm<TIO>(Vt + (c * 16 + l16) * VT_LD + 32 * kc, lg);
-            S[c][m] = mma32(op.k[m][kc], fv, S[c][m]);
+            sn = mma32(op.k[m][kc], fv, sn);
           }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) S[c][m][j] = live ? sn[j] : S[c][m][j];
         }
-#pragma unroll
-      for (int c = 0; c < NJ; ++c)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) S[c][m][j] = live ? S[c][m][j] : s_keep[c][m][j];
     }
+    publish(lds, S, active);
     if (nxt) {
       load_kg<ALL>(op, *nxt);
       op.start = nxt_ent->start;
       op.len = nxt_ent->len;
     }
+    __syncthreads();
   }
 
   // Token slots past the chunk's tiles (C < 32) must read as zero.

@@ -274,6 +274,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(S[c][m][j]));
+  SS::publish(lds, S, true);  // read by the first step after the barrier below
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const int64_t ostride = (int64_t)n_heads * D;
@@ -525,6 +526,7 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
     if (!s_ok) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     SS::clear_vt(lds);  // the chunk-local stage used this LDS
+    SS::publish(lds, S, w < Gm::KBD);
     if (s0 == 0) SS::template load<false>(cur, slot_out(0), jb);
     __syncthreads();
     for (int s = s0; s < s1; ++s) {
@@ -534,10 +536,12 @@ __global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
       SS::template step<false, kLocalThreads>(lds, S, cur, o, ostride, cc.h, jb);
       cur = nxt;
       ++cc.ci;
-      if (cc.ci >= cc.ce) {  // task finished
+      if (cc.ci >= cc.ce) {  // task finished (uniform over the workgroup)
         state_out();
         cursor_task(cc, cc.i + 1, team, a);
         enter_tasks();
+        SS::publish(lds, S, w < Gm::KBD);  // the next task's start state
+        __syncthreads();
       }
     }
     // release the round's slots: every wave's reads are complete
