@@ -203,8 +203,8 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
 // the width (more MFMA and LDS work per workgroup between barriers), while the
 // L2 traffic for the shared operators shrinks with it; measured on MI355X at
 // H = 32, d = 128, C = 64 (ms of the scan stage):
-//     one 32k sequence:   NJ 1: 0.62   NJ 2: 0.83   NJ 4: 1.42
-//     four 32k sequences: NJ 1: 2.44   NJ 2: 1.67   NJ 4: 1.56
+//     one 32k sequence:   NJ 1: 0.59   NJ 2: 0.69   NJ 4: 1.04
+//     four 32k sequences: NJ 1: 2.24   NJ 2: 1.48   NJ 4: 1.30
 // A single sequence is bound by its chain of steps, a batch by the shared
 // traffic.  The launch takes the widest block that still leaves every CU at
 // least one workgroup (bf16 only: the fp32 fragments are twice the registers).
