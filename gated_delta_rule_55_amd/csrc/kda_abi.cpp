@@ -57,15 +57,17 @@ int check_gate(const kda_gate_desc& gt, const float* g, bool work, int64_t rows,
   r[0] = r[1] = r[2] = Range{0, 0};
   if (gt.mode == KDA_GATE_GIVEN) {
     if (work && !g) return KDA_ERR_NULL;
-    if (g && !aligned(g, 4)) return KDA_ERR_ALIGN;
+    if (g && !aligned(g, 16)) return KDA_ERR_ALIGN;  // read as 16-byte vectors
     r[0] = range_of(g, rows * H * D * 4);
     *out = kda::GateArgs{};
     return KDA_OK;
   }
   if (gt.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
   if (work && (!gt.x || !gt.a_log || !gt.dt_bias)) return KDA_ERR_NULL;
-  if ((gt.x && !aligned(gt.x, (uintptr_t)es)) || (gt.a_log && !aligned(gt.a_log, 4)) ||
-      (gt.dt_bias && !aligned(gt.dt_bias, 4)))
+  // x and dt_bias are read as vectors, a_log element-wise
+  (void)es;
+  if ((gt.x && !aligned(gt.x, 16)) || (gt.a_log && !aligned(gt.a_log, 4)) ||
+      (gt.dt_bias && !aligned(gt.dt_bias, 16)))
     return KDA_ERR_ALIGN;
   r[0] = range_of(gt.x, rows * H * D * es);
   r[1] = range_of(gt.a_log, H * 4);
@@ -133,13 +135,16 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
 int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range (&rin)[10]) {
   if (!d->cu_seqlens && d->n_seqs != 1) return KDA_ERR_NULL;
   if (d->t_total > 0 && (!d->q || !d->k || !d->v || !d->beta || !d->o)) return KDA_ERR_NULL;
-  // q and k rows are read as 16-byte vectors; everything else element-wise.
+  // q, k, v rows and the states are read as 16-byte vectors; beta, o and
+  // the index tables element-wise.
   const uintptr_t es_al = d->dtype == KDA_DTYPE_BF16 ? 2 : 4;
-  if ((d->q && !aligned(d->q, 16)) || (d->k && !aligned(d->k, 16))) return KDA_ERR_ALIGN;
-  const void* pe[] = {d->v, d->beta, d->o};
+  const void* p16[] = {d->q, d->k, d->v, d->h0, d->ht};
+  for (const void* p : p16)
+    if (p && !aligned(p, 16)) return KDA_ERR_ALIGN;
+  const void* pe[] = {d->beta, d->o};
   for (const void* p : pe)
     if (p && !aligned(p, es_al)) return KDA_ERR_ALIGN;
-  const void* p4[] = {d->h0, d->ht, d->cu_seqlens, d->state_indices};
+  const void* p4[] = {d->cu_seqlens, d->state_indices};
   for (const void* p : p4)
     if (p && !aligned(p, 4)) return KDA_ERR_ALIGN;
 
@@ -356,10 +361,11 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   if (d->n_seqs == 0) return KDA_OK;
   if (!d->state || !d->q || !d->k || !d->v || !d->beta || !d->o) return KDA_ERR_NULL;
   const bool bf = d->dtype == KDA_DTYPE_BF16;
-  // the state is read and written as 16-byte vectors; the rest element-wise
-  if (!aligned(d->state, 16)) return KDA_ERR_ALIGN;
+  // the state, q and k are read as 16-byte vectors (q, k as pieces of four
+  // elements); v, beta, o element-wise
+  if (!aligned(d->state, 16) || !aligned(d->q, 16) || !aligned(d->k, 16)) return KDA_ERR_ALIGN;
   if (d->state_indices && !aligned(d->state_indices, 4)) return KDA_ERR_ALIGN;
-  const void* pe[] = {d->q, d->k, d->v, d->beta, d->o};
+  const void* pe[] = {d->v, d->beta, d->o};
   for (const void* p : pe)
     if (!aligned(p, bf ? 2 : 4)) return KDA_ERR_ALIGN;
   const int64_t es = bf ? 2 : 4, NH = (int64_t)d->n_seqs * d->n_heads, D = d->dk;

@@ -23,33 +23,31 @@
 
 namespace kda {
 
-// One wave: k . q and, when the rows are to be L2-normalised, the factors
-// 1/sqrt(|k|^2 + eps) and 1/sqrt(|q|^2 + eps) (else 1).  The kernels use the
-// raw rows and apply the factors to the reductions they feed: k . q, S^T k,
-// S^T q and the rank-one write k u^T.
-template <int D>
-__device__ __forceinline__ void qk_dots(const float* sk, const float* sq, int norm, float* kq,
-                                        float* rk, float* rq) {
-  const int lane = threadIdx.x & 63;
-  float a = 0.f, kk = 0.f, qq = 0.f;
-  for (int i = lane; i < D; i += 64) {
-    a += sk[i] * sq[i];
-    kk += sk[i] * sk[i];
-    qq += sq[i] * sq[i];
+// One token's k and q rows held as 4 consecutive elements by each of NQ =
+// D / 4 consecutive lanes (NQ divides 64): scale both rows in place to unit
+// norm when normalising (x / sqrt(sum x^2 + eps)) and return k . q of the rows
+// as used.  Sums are reduced across the NQ lanes with xor shuffles, so every
+// lane of the row gets them; every lane of the wave must call it.
+template <int NQ>
+__device__ __forceinline__ float row_prepare(f32x4& k4, f32x4& q4, int norm) {
+  float kk = 0.f, qq = 0.f, kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    kk += k4[e] * k4[e];
+    qq += q4[e] * q4[e];
+    kq += k4[e] * q4[e];
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    a += __shfl_xor(a, off, 64);
+  for (int off = 1; off < NQ; off <<= 1) {
     kk += __shfl_xor(kk, off, 64);
     qq += __shfl_xor(qq, off, 64);
+    kq += __shfl_xor(kq, off, 64);
   }
-  if (lane == 0) {
-    const float fk = norm ? __builtin_amdgcn_rsqf(kk + kQkNormEps) : 1.f;
-    const float fq = norm ? __builtin_amdgcn_rsqf(qq + kQkNormEps) : 1.f;
-    *kq = a * fk * fq;
-    *rk = fk;
-    *rq = fq;
-  }
+  const float fk = norm ? __builtin_amdgcn_rsqf(kk + kQkNormEps) : 1.f;
+  const float fq = norm ? __builtin_amdgcn_rsqf(qq + kQkNormEps) : 1.f;
+  k4 *= fk;
+  q4 *= fq;
+  return kq * fk * fq;
 }
 
 // GATE: the decay comes from the raw gate x with a_log and dt_bias (the Kimi
@@ -74,7 +72,8 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 
   __shared__ float s_q[D], s_k[D], s_d[D], s_u[D];
   __shared__ float s_red[2][RG][D];
-  __shared__ float s_kq, s_rk, s_rq;  // k.q (normalised), 1/|k|, 1/|q| (1 without norm)
+  __shared__ float s_kq;
+  using V4 = typename Vec4<TIO>::type;
 
   const int tid = threadIdx.x;
   const int cq = tid % NQ;
@@ -98,19 +97,38 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 
   // key head of value head h: h / (n_heads / kheads), rows of kheads heads
   const int64_t qk_row = (nh / n_heads) * kheads + (nh % n_heads) / (n_heads / kheads);
-  if (tid < D) {
-    s_q[tid] = to_f32(q[qk_row * D + tid]);
-    s_k[tid] = to_f32(k[qk_row * D + tid]);
-    if constexpr (GATE) {
-      const int h = (int)(nh % n_heads);
-      s_d[tid] = fast_exp2(kimi_gate_log2(to_f32(gx[nh * D + tid]) + dt_bias[h * D + tid],
-                                          __expf(a_log[h])));
-    } else {
-      s_d[tid] = __expf(g[nh * D + tid]);
+  const int h = (int)(nh % n_heads);
+  // wave 0 stages the token's rows, four elements per lane (lanes past NQ
+  // repeat the row and store nothing); q and k leave normalised when asked
+  if (tid < 64) {
+    const V4 qv = *reinterpret_cast<const V4*>(q + qk_row * D + 4 * cq);
+    const V4 kv = *reinterpret_cast<const V4*>(k + qk_row * D + 4 * cq);
+    f32x4 q4, k4, d4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q4[e] = to_f32(qv[e]);
+      k4[e] = to_f32(kv[e]);
     }
+    if constexpr (GATE) {
+      const V4 xv = *reinterpret_cast<const V4*>(gx + nh * D + 4 * cq);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(dt_bias + h * D + 4 * cq);
+      const float ea = __expf(a_log[h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d4[e] = fast_exp2(kimi_gate_log2(to_f32(xv[e]) + b4[e], ea));
+    } else {
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(g + nh * D + 4 * cq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) d4[e] = __expf(g4[e]);
+    }
+    const float kq = row_prepare<NQ>(k4, q4, qk_norm);
+    if (tid < NQ) {
+      *reinterpret_cast<f32x4*>(&s_q[4 * cq]) = q4;
+      *reinterpret_cast<f32x4*>(&s_k[4 * cq]) = k4;
+      *reinterpret_cast<f32x4*>(&s_d[4 * cq]) = d4;
+    }
+    if (tid == 0) s_kq = kq;
   }
   __syncthreads();
-  if (tid < 64) qk_dots<D>(s_k, s_q, qk_norm, &s_kq, &s_rk, &s_rq);
 
   f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
@@ -131,8 +149,6 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
       p += s_red[0][j][tid];
       r += s_red[1][j][tid];
     }
-    p *= s_rk;
-    r *= s_rq;
     const float b = to_f32(beta[nh]);
     const float u = b * (to_f32(v[nh * D + tid]) - p);
     s_u[tid] = u;
@@ -140,7 +156,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
   }
   __syncthreads();
 
-  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]) * s_rk;
+  const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
@@ -155,9 +171,15 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 // recurrent op (page "model(kimi_linear): ONE-SURFACE ROW 7 -- fold
 // Kimi-Linear onto the shared paged runner", B2: KdaGatedDeltaRule for decode
 // and continuing prefills over the state pool keyed by state indices).
-// One 256-thread workgroup per (sequence, head), tiled like decode_kernel;
-// token t + 1's inputs are loaded while token t computes.  cu_seqlens is read
-// clamped to [0, t_total], so any contents stay in bounds.
+// One 256-thread workgroup per (sequence, head), tiled like decode_kernel.
+// Tokens go in blocks of B = 1024 / D: each thread loads one 4-element piece
+// of q, k, v and the decay input of one token of a block (a block is exactly
+// one such load per thread), and the next block's loads are issued when a
+// block starts, so they have the whole block's work to arrive in.  A block is
+// staged in LDS as fp32 (decay already exp'd) and its tokens run from there
+// with two barriers each; a block at the sequence's end runs only its real
+// tokens.  cu_seqlens is read clamped to [0, t_total], so any contents stay
+// in bounds.
 template <typename TIO, int D, bool GATE>
 __global__ __launch_bounds__(256) void recurrent_kernel(
     const float* __restrict__ h0, float* __restrict__ ht, const TIO* __restrict__ q,
@@ -169,11 +191,13 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   constexpr int NQ = D / 4;
   constexpr int RG = 256 / NQ;
   constexpr int RPT = D / RG;
+  constexpr int B = 256 / NQ;  // tokens per block: one 4-element piece per thread
   static_assert(NQ * RG == 256 && RG * RPT == D, "recurrent tiling");
+  using V4 = typename Vec4<TIO>::type;
 
-  __shared__ float s_q[2][D], s_k[2][D], s_d[2][D], s_v[2][D], s_u[D];
+  __shared__ float s_q[B][D], s_k[B][D], s_d[B][D], s_v[B][D], s_b[B], s_kq[B];
+  __shared__ float s_u[D];
   __shared__ float s_red[2][RG][D];
-  __shared__ float s_kq, s_rk, s_rq, s_b[2];
 
   const int tid = threadIdx.x;
   const int cq = tid % NQ;
@@ -189,74 +213,102 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   t1 = t1 < t0 ? t0 : (t1 > t_total ? t_total : t1);
   const int64_t sb = ((int64_t)slot * n_heads + h) * (int64_t)(D * D);
 
+  // no h0: an empty buffer whose loads read 0 (no branch around the loads)
+  const __amdgpu_buffer_rsrc_t hr =
+      make_rsrc(const_cast<float*>(h0 ? h0 + sb : h0), h0 ? D * D * 4 : 0);
   f32x4 s[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
-    s[i] = h0 ? *reinterpret_cast<const f32x4*>(h0 + sb + (rg + RG * i) * D + 4 * cq) : zero4();
+    s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         hr, ((rg + RG * i) * D + 4 * cq) * 4, 0, 0));
 
+  // this thread's piece of a block: token rg of the block, elements 4cq..4cq+3
   const float ea = GATE ? __expf(a_log[h]) : 1.f;
-  const float bias_c = (GATE && tid < D) ? dt_bias[h * D + tid] : 0.f;
-  // this thread's element of one token (tid < D), loaded ahead
-  TIO rq{}, rk{}, rv{}, rx{}, rb{};
-  float rg_{};
+  f32x4 bias4 = zero4();
+  if constexpr (GATE) bias4 = *reinterpret_cast<const f32x4*>(dt_bias + h * D + 4 * cq);
   const int kh = h / (n_heads / kheads);  // key head of value head h
-  auto fetch = [&](int64_t t) {
-    if (tid < D) {
-      const int64_t at = (t * n_heads + h) * D + tid;
-      const int64_t akt = (t * kheads + kh) * D + tid;
-      rq = q[akt];
-      rk = k[akt];
-      rv = v[at];
-      if constexpr (GATE) rx = gx[at];
-      else rg_ = g[at];
-    }
-    if (tid == 0) rb = beta[t * n_heads + h];
+  V4 lq, lk, lv, lx;
+  f32x4 lg = zero4();
+  TIO lb;
+  auto fetch = [&](int64_t tb) {  // the block starting at tb (t0 <= tb < t1)
+    const int64_t t = tb + rg < t1 ? tb + rg : t1 - 1;
+    const int64_t at = (t * n_heads + h) * D + 4 * cq;
+    const int64_t akt = (t * kheads + kh) * D + 4 * cq;
+    lq = *reinterpret_cast<const V4*>(q + akt);
+    lk = *reinterpret_cast<const V4*>(k + akt);
+    lv = *reinterpret_cast<const V4*>(v + at);
+    if constexpr (GATE) lx = *reinterpret_cast<const V4*>(gx + at);
+    else lg = *reinterpret_cast<const f32x4*>(g + at);
+    lb = beta[t * n_heads + h];
   };
-  if (t0 < t1) fetch(t0);
-  for (int64_t t = t0; t < t1; ++t) {
-    const int pb = (int)(t & 1);
-    if (tid < D) {
-      s_q[pb][tid] = to_f32(rq);
-      s_k[pb][tid] = to_f32(rk);
-      s_v[pb][tid] = to_f32(rv);
-      if constexpr (GATE) s_d[pb][tid] = fast_exp2(kimi_gate_log2(to_f32(rx) + bias_c, ea));
-      else s_d[pb][tid] = __expf(rg_);
-    }
-    if (tid == 0) s_b[pb] = to_f32(rb);
-    __syncthreads();
-    if (t + 1 < t1) fetch(t + 1);
-    if (tid < 64) qk_dots<D>(s_k[pb], s_q[pb], qk_norm, &s_kq, &s_rk, &s_rq);
-    f32x4 pk = zero4(), pq = zero4();
+  // stage the fetched block: q and k rows normalised when asked (the NQ lanes
+  // of a row reduce its sums together), k . q per token, decay exp'd (rows
+  // past the sequence's end repeat its last token and are never used)
+  auto stage = [&](int64_t /*tb*/) {
+    f32x4 q4, k4, v4, d4;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
-      s[i] *= s_d[pb][r];
-      pk += s[i] * s_k[pb][r];
-      pq += s[i] * s_q[pb][r];
+    for (int e = 0; e < 4; ++e) {
+      q4[e] = to_f32(lq[e]);
+      k4[e] = to_f32(lk[e]);
+      v4[e] = to_f32(lv[e]);
+      float d;
+      if constexpr (GATE) d = fast_exp2(kimi_gate_log2(to_f32(lx[e]) + bias4[e], ea));
+      else d = __expf(lg[e]);
+      d4[e] = d;
     }
-    *reinterpret_cast<f32x4*>(&s_red[0][rg][4 * cq]) = pk;
-    *reinterpret_cast<f32x4*>(&s_red[1][rg][4 * cq]) = pq;
-    __syncthreads();
-    if (tid < D) {
-      float p = 0.f, r = 0.f;
+    const float kq = row_prepare<NQ>(k4, q4, qk_norm);
+    *reinterpret_cast<f32x4*>(&s_q[rg][4 * cq]) = q4;
+    *reinterpret_cast<f32x4*>(&s_k[rg][4 * cq]) = k4;
+    *reinterpret_cast<f32x4*>(&s_v[rg][4 * cq]) = v4;
+    *reinterpret_cast<f32x4*>(&s_d[rg][4 * cq]) = d4;
+    if (cq == 0) {
+      s_b[rg] = to_f32(lb);
+      s_kq[rg] = kq;
+    }
+  };
+  if (t0 < t1) {
+    fetch(t0);
+    stage(t0);
+  }
+  __syncthreads();
+  for (int64_t tb = t0; tb < t1; tb += B) {
+    fetch(tb + B < t1 ? tb + B : tb);  // the next block (the current one again at the end)
+    const int nb = t1 - tb < B ? (int)(t1 - tb) : B;  // tokens of this block (uniform)
+#pragma unroll 1
+    for (int j = 0; j < nb; ++j) {
+      f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
-      for (int j = 0; j < RG; ++j) {
-        p += s_red[0][j][tid];
-        r += s_red[1][j][tid];
+      for (int i = 0; i < RPT; ++i) {
+        const int r = rg + RG * i;
+        s[i] *= s_d[j][r];
+        pk += s[i] * s_k[j][r];
+        pq += s[i] * s_q[j][r];
       }
-      p *= s_rk;
-      r *= s_rq;
-      const float u = s_b[pb] * (s_v[pb][tid] - p);
-      s_u[tid] = u;
-      o[(t * n_heads + h) * D + tid] = from_f32<TIO>(scale * (r + s_kq * u));
-    }
-    __syncthreads();
-    const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]) * s_rk;
+      *reinterpret_cast<f32x4*>(&s_red[0][rg][4 * cq]) = pk;
+      *reinterpret_cast<f32x4*>(&s_red[1][rg][4 * cq]) = pq;
+      __syncthreads();
+      if (tid < D) {
+        float p = 0.f, r = 0.f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
-      s[i] += s_k[pb][r] * u4;
+        for (int jj = 0; jj < RG; ++jj) {
+          p += s_red[0][jj][tid];
+          r += s_red[1][jj][tid];
+        }
+        const float u = s_b[j] * (s_v[j][tid] - p);
+        s_u[tid] = u;
+        o[((tb + j) * n_heads + h) * D + tid] = from_f32<TIO>(scale * (r + s_kq[j] * u));
+      }
+      __syncthreads();
+      const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = rg + RG * i;
+        s[i] += s_k[j][r] * u4;
+      }
     }
+    __syncthreads();  // every token of the block has read it
+    if (tb + B < t1) stage(tb + B);
+    __syncthreads();
   }
   if (ht) {
 #pragma unroll

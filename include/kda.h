@@ -34,8 +34,10 @@
  *     failed kernel launch returns KDA_ERR_HIP (kda_last_hip_error() has the
  *     hipError_t).  NaN/Inf in the data propagate; data is not inspected.
  *   - Tensors are dense row-major with the last index contiguous.  Alignment:
- *     prefill q and k, and the decode state, 16 bytes (read as 16-byte
- *     vectors); every other pointer, its element size.
+ *     16 bytes for everything read as vectors: q, k, v, g, the raw gate x,
+ *     dt_bias, h0 and ht of a prefill; the state, q, k, g, x and dt_bias of
+ *     a decode step.  Every other pointer (beta, o, a_log, the decode v, the
+ *     index tables), its element size.
  *   - Supported: dk = dv = d in {32, 64, 128}; chunk in {16, 32, 64};
  *     dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16 for q, k, v, beta and o.
  *     g, h0, ht and the decode state are always fp32.

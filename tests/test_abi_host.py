@@ -108,6 +108,7 @@ def test_workspace_query_sizes(abi):
 @pytest.mark.parametrize("over,status", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(n_seqs=2), -1),   # cu_seqlens NULL, N > 1
     (dict(q=0x100008), -5), (dict(g=0x400002), -5),
+    (dict(v=0x300008), -5), (dict(g=0x400004), -5), (dict(h0=0x700008), -5),  # vector reads
     (dict(o=0x100000 + 64), -9),                                      # o overlaps q
     (dict(h0=0x700000, ht=0x700000 + 16), -9),                        # ht partly overlaps h0
 ])
@@ -198,6 +199,7 @@ def test_prefill_rejects_small_or_missing_workspace(abi):
 @pytest.mark.parametrize("over,status", [
     (dict(struct_size=4), -8), (dict(dtype=9), -3), (dict(n_heads=0), -2), (dict(n_seqs=-1), -2),
     (dict(dk=64, dv=128), -4), (dict(state=None), -1), (dict(state=0x100008), -5),
+    (dict(q=0x900008), -5), (dict(g=0xc00004), -5),
     (dict(o=0x100000), -9),
 ])
 def test_decode_validation(abi, over, status):
