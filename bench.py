@@ -8,6 +8,14 @@ the recurrent decode leg: batch 64, 32 heads, d = 128, 256 successive
 one-token steps on a carried state produced by a chunked prefill of 1024
 tokens per sequence.
 
+Further legs beside it: the prefill with the gate activation fused, a
+continuing prefill (16 new tokens per sequence through the recurrent op), and
+the short causal conv (forward over the prefill-32k tokens, one-token update
+at the decode shape).  Decode steps and conv updates are also captured once in
+a graph and replayed (each replay checked bit for bit against the eager run):
+the replay time is the kernels' own, the eager time beside it includes the
+per-call host cost of issuing them one by one from Python.
+
 Prints one JSON line.  `value` is prefill tokens/s with inputs resident in HBM.
 The roofline entry prices the prefill against HBM bandwidth with the
 algorithmic bytes of the pass (q, k, v, g, beta read once, o written once, h0
@@ -28,6 +36,9 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+# The CPU oracle (OpenMP) runs last; its idle threads sleep instead of
+# spinning on the cores the GPU legs' host thread uses.
+os.environ.setdefault("OMP_WAIT_POLICY", "PASSIVE")
 
 METRIC = "KDA prefill tokens/s (H=32,d=128,T=32k) + decode steps/s; % of roofline"
 HBM_PEAK_GBS = 8000.0
@@ -167,18 +178,42 @@ def bench_decode(args, torch, kda, synth):
 
     state.copy_(state0)
     steps()  # warm-up
-    times = []
+    eager = []
     for _ in range(args.decode_reps):
         state.copy_(state0)  # restore, untimed
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        steps()
+        steps()  # issued from Python, one call per step
+        b.record(stream)
+        torch.cuda.synchronize()
+        eager.append(a.elapsed_time(b))
+    out_ref, state_ref = out.clone(), state.clone()
+    # The S steps captured once in a graph and replayed, as a serving loop
+    # issues decode: the kernels' own time, without per-call host cost.  Each
+    # replay is checked bit for bit against the eager run.
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            steps()
+    times = []
+    for _ in range(max(3, args.decode_reps)):
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
         b.record(stream)
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b))
+        if not (torch.equal(state, state_ref) and torch.equal(out, out_ref)):
+            raise RuntimeError("graph replay of the decode steps differs from the eager run")
     ms = statistics.median(times)
     rec = bench_recurrent(args, torch, kda, inp, state0, dec, stream)
+    rec["eager_decode_ms_per_step"] = round(statistics.median(eager) / S, 5)
     return inp, S, ms, dec, rec
 
 
@@ -276,27 +311,61 @@ def bench_conv(args, torch, kda, T=32768, N_dec=64, reps=10, dec_calls=256):
     del x, outs
     # decode shape: one token for each of 64 sequences per call
     xd = torch.randn((dec_calls, N_dec, dim), generator=gen, device="cuda").to(torch.bfloat16)
-    pool = torch.randn((N_dec, W - 1, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    pool0 = torch.randn((N_dec, W - 1, dim), generator=gen, device="cuda").to(torch.bfloat16)
+    pool = pool0.clone()
     slots = torch.arange(N_dec, dtype=torch.int32, device="cuda")
     yd = tuple(torch.empty((N_dec, dim // 3), dtype=torch.bfloat16, device="cuda")
                for _ in range(3))
-    for i in range(3):
-        kda.causal_conv1d_update(xd[i], w, b, pool, state_indices=slots, split=(dim // 3,) * 3,
-                                 out=yd)
+
+    def updates():
+        for i in range(dec_calls):
+            kda.causal_conv1d_update(xd[i], w, b, pool, state_indices=slots,
+                                     split=(dim // 3,) * 3, out=yd)
+
+    updates()  # warm-up
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
     a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0 = time.perf_counter()
     a.record(stream)
-    for i in range(dec_calls):
-        kda.causal_conv1d_update(xd[i], w, b, pool, state_indices=slots, split=(dim // 3,) * 3,
-                                 out=yd)
+    updates()  # issued from Python, one call at a time
     e.record(stream)
     torch.cuda.synchronize()
-    ums = a.elapsed_time(e) / dec_calls
+    host_us = (time.perf_counter() - h0) * 1e6 / dec_calls
+    eager_us = a.elapsed_time(e) * 1e3 / dec_calls
+    y_ref = tuple(t.clone() for t in yd)
+    pool_ref = pool.clone()
+    # The same calls captured once in a graph and replayed: the kernels' own
+    # time, without the per-call host cost.  Every replay is checked against
+    # the eager run.
+    graph = torch.cuda.CUDAGraph()
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            updates()
+    times = []
+    for _ in range(3):
+        pool.copy_(pool0)
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+        if not (torch.equal(pool, pool_ref) and all(torch.equal(x, r) for x, r in zip(yd, y_ref))):
+            raise RuntimeError("graph replay of the conv updates differs from the eager run")
+    ums = statistics.median(times) / dec_calls
     ubytes = 2 * N_dec * dim * 2 + 2 * N_dec * (W - 1) * dim * 2 + dim * (W + 1) * 4
     uach = ubytes / (ums / 1e3) / 1e9
     res["update"] = {
         "workload": f"causal conv one-token update: {N_dec} sequences, dim={dim}, W={W}, SiLU, "
-                    f"bf16, {N_dec}-slot tap pool; {dec_calls} back-to-back calls",
+                    f"bf16, {N_dec}-slot tap pool; {dec_calls} calls replayed from a captured "
+                    "graph (checked bitwise against the eager run)",
         "us_per_call": round(ums * 1e3, 2),
+        "eager_us_per_call": round(eager_us, 2), "eager_host_us_per_call": round(host_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(uach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(uach / HBM_PEAK_GBS, 4), "traffic": None,
                      "scope": f"{ubytes} bytes per call; launch-bound at this size"}}
@@ -423,8 +492,10 @@ def main():
         dach = dbytes / (step_ms / 1e3) / 1e9
         line["decode"] = {
             "workload": "decode-64x256: batch 64, H=32, d=128, 256 steps on a state from a "
-                        "64 x 1024-token chunked prefill",
+                        "64 x 1024-token chunked prefill, the steps replayed from a captured "
+                        "graph (checked bitwise against the eager run)",
             "steps_per_s": round(1e3 / step_ms, 1), "ms_per_step": round(step_ms, 5),
+            "eager_ms_per_step": rec.pop("eager_decode_ms_per_step"),
             "tokens_per_s": round(64 * 1e3 / step_ms, 1),
             "roofline": {"bound": "hbm", "achieved": round(dach, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
@@ -432,13 +503,16 @@ def main():
                          "note": "the 134 MB state fits the 256 MB Infinity Cache"},
         }
         line["recurrent_prefill"] = rec
-        if not args.no_cpu:
-            log("timing the CPU oracle (decode)")
-            line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)
-        del dec
     if not args.no_conv:
         log("causal conv leg")
         line["causal_conv"] = bench_conv(args, torch, kda)
+    # CPU baselines last: the oracle's OpenMP threads must not compete with
+    # the host thread that issues the GPU legs
+    if not args.no_decode and not args.no_cpu:
+        log("timing the CPU oracle (decode)")
+        line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)
+    if not args.no_decode:
+        del dec
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")
