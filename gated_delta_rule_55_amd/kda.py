@@ -276,9 +276,9 @@ def _conv_args(x, weight, bias, state_in, state_out, state_indices, n_seqs, spli
                 S = int(st.shape[0])
             _check(st, name, (S, W - 1, dim), x.dtype, dev)
     if state_indices is not None:
+        if state_in is None and state_out is None:
+            raise ValueError("state_indices needs a tap pool (state_in and/or state_out)")
         _check(state_indices, "state_indices", (n_seqs,), torch.int32, dev)
-        if S is None:
-            S = 1  # no state buffer: the slots only select which sequences run
     widths = (dim,) if split is None else tuple(int(w) for w in split)
     if sum(widths) != dim or not 1 <= len(widths) <= 3:
         raise ValueError(f"split {widths} must be 1..3 widths summing to dim={dim}")
