@@ -8,7 +8,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkda.so")
 
-KDA_ABI_VERSION = 4
+KDA_ABI_VERSION = 5
 KDA_OK = 0
 KDA_ERR_NULL = -1
 KDA_ERR_SHAPE = -2
@@ -71,6 +71,7 @@ class PrefillDesc(ctypes.Structure):
         ("n_slots", ctypes.c_int32),
         ("n_k_heads", ctypes.c_int32),
         ("qk_l2norm", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
     ]
 
 
@@ -95,6 +96,7 @@ class DecodeDesc(ctypes.Structure):
         ("n_slots", ctypes.c_int32),
         ("n_k_heads", ctypes.c_int32),
         ("qk_l2norm", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
     ]
 
 

@@ -39,6 +39,18 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.l
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 
+// State dtype: 0 or fp32, or bf16 with bf16 inputs.  Sets *bf16_state.
+int check_state_dtype(int32_t state_dtype, int32_t dtype, bool* bf16_state) {
+  if (state_dtype == 0 || state_dtype == KDA_DTYPE_F32) {
+    *bf16_state = false;
+    return KDA_OK;
+  }
+  if (state_dtype != KDA_DTYPE_BF16) return KDA_ERR_DTYPE;
+  if (dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+  *bf16_state = true;
+  return KDA_OK;
+}
+
 // Key heads (0 = H, else a divisor of H) and the q/k normalisation flag.
 int check_qk(int32_t n_k_heads, int32_t qk_l2norm, int H, kda::QkArgs* out) {
   const int hg = n_k_heads == 0 ? H : n_k_heads;
@@ -108,6 +120,8 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
   if (chunked && d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
   const int sq = check_qk(d->n_k_heads, d->qk_l2norm, d->n_heads, &a->qk);
   if (sq != KDA_OK) return sq;
+  const int sd = check_state_dtype(d->state_dtype, d->dtype, &a->state_bf16);
+  if (sd != KDA_OK) return sd;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
   a->plan = d->plan;
   a->n_seqs = d->n_seqs;
@@ -156,11 +170,12 @@ int check_prefill_pointers(const kda_prefill_desc* d, kda::PrefillArgs* a, Range
   const int st = check_gate(d->gate, d->g, T > 0, T, H, D, es, &a->gate, rgate);
   if (st != KDA_OK) return st;
   const int64_t HG = a->qk.kheads;
+  const int64_t ess = a->state_bf16 ? 2 : 4;  // bytes per state element
   const Range rq = range_of(d->q, T * HG * D * es), rk = range_of(d->k, T * HG * D * es),
               rv = range_of(d->v, T * H * D * es), rb = range_of(d->beta, T * H * es),
               ro = range_of(d->o, T * H * D * es),
-              rh0 = range_of(d->h0, d->h0 ? N * H * D * D * 4 : 0),
-              rht = range_of(d->ht, d->ht ? N * H * D * D * 4 : 0),
+              rh0 = range_of(d->h0, d->h0 ? N * H * D * D * ess : 0),
+              rht = range_of(d->ht, d->ht ? N * H * D * D * ess : 0),
               rcu = range_of(d->cu_seqlens, d->cu_seqlens ? ((int64_t)d->n_seqs + 1) * 4 : 0),
               rsi = range_of(d->state_indices, d->state_indices ? (int64_t)d->n_seqs * 4 : 0);
   const Range inputs[10] = {rq, rk, rv, rgate[0], rgate[1], rgate[2], rb, rh0, rcu, rsi};
@@ -314,7 +329,7 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
   for (const Range& r : rin)
     if (overlap(rw, r)) return KDA_ERR_ALIAS;
   if (overlap(rw, range_of(d->o, T * H * D * es)) ||
-      overlap(rw, range_of(d->ht, d->ht ? N * H * D * D * 4 : 0)))
+      overlap(rw, range_of(d->ht, d->ht ? N * H * D * D * (a.state_bf16 ? 2 : 4) : 0)))
     return KDA_ERR_ALIAS;
   return hip_status(kda::launch_prefill(a, workspace, (hipStream_t)stream,
                                         reinterpret_cast<const hipEvent_t*>(events)));
@@ -358,6 +373,8 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   kda::DecodeArgs a;
   const int sq = check_qk(d->n_k_heads, d->qk_l2norm, d->n_heads, &a.qk);
   if (sq != KDA_OK) return sq;
+  const int sd = check_state_dtype(d->state_dtype, d->dtype, &a.state_bf16);
+  if (sd != KDA_OK) return sd;
   if (d->n_seqs == 0) return KDA_OK;
   if (!d->state || !d->q || !d->k || !d->v || !d->beta || !d->o) return KDA_ERR_NULL;
   const bool bf = d->dtype == KDA_DTYPE_BF16;
@@ -375,7 +392,8 @@ int kda_recurrent_decode(const kda_decode_desc* d, void* stream) {
   if (st != KDA_OK) return st;
   const Range ro = range_of(d->o, NH * D * es);
   const int64_t NS = (d->state_indices ? (int64_t)d->n_slots : (int64_t)d->n_seqs) * d->n_heads;
-  const Range ins[] = {range_of(d->state, NS * D * D * 4), range_of(d->q, NHG * D * es),
+  const Range ins[] = {range_of(d->state, NS * D * D * (a.state_bf16 ? 2 : 4)),
+                       range_of(d->q, NHG * D * es),
                        range_of(d->k, NHG * D * es),       range_of(d->v, NH * D * es),
                        rgate[0], rgate[1], rgate[2],       range_of(d->beta, NH * es),
                        range_of(d->state_indices, d->state_indices ? (int64_t)d->n_seqs * 4 : 0)};

@@ -52,8 +52,9 @@ __device__ __forceinline__ float row_prepare(f32x4& k4, f32x4& q4, int norm) {
 
 // GATE: the decay comes from the raw gate x with a_log and dt_bias (the Kimi
 // gate, see kimi_gate_log2) instead of a given g.
-template <typename TIO, int D, bool GATE>
-__global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
+// TS: storage type of the state (fp32, or bf16 rounded once per step).
+template <typename TIO, int D, bool GATE, typename TS>
+__global__ __launch_bounds__(256) void decode_kernel(TS* __restrict__ state,
                                                      const TIO* __restrict__ q,
                                                      const TIO* __restrict__ k,
                                                      const TIO* __restrict__ v,
@@ -87,13 +88,12 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
     if (slot < 0 || slot >= n_slots) return;
     sh = (int64_t)slot * n_heads + nh % n_heads;
   }
-  float* S = state + sh * (int64_t)(D * D);
+  TS* S = state + sh * (int64_t)(D * D);
 
   // Issue every state load first: rows rg + RG * i, columns 4cq .. 4cq + 3.
   f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    s[i] = *reinterpret_cast<const f32x4*>(S + (rg + RG * i) * D + 4 * cq);
+  for (int i = 0; i < RPT; ++i) s[i] = load_state4(S + (rg + RG * i) * D + 4 * cq);
 
   // key head of value head h: h / (n_heads / kheads), rows of kheads heads
   const int64_t qk_row = (nh / n_heads) * kheads + (nh % n_heads) / (n_heads / kheads);
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const int r = rg + RG * i;
-    *reinterpret_cast<f32x4*>(S + r * D + 4 * cq) = s[i] + s_k[r] * u4;
+    store_state4(S + r * D + 4 * cq, s[i] + s_k[r] * u4);
   }
 }
 
@@ -180,9 +180,9 @@ __global__ __launch_bounds__(256) void decode_kernel(float* __restrict__ state,
 // with two barriers each; a block at the sequence's end runs only its real
 // tokens.  cu_seqlens is read clamped to [0, t_total], so any contents stay
 // in bounds.
-template <typename TIO, int D, bool GATE>
+template <typename TIO, int D, bool GATE, typename TS>
 __global__ __launch_bounds__(256) void recurrent_kernel(
-    const float* __restrict__ h0, float* __restrict__ ht, const TIO* __restrict__ q,
+    const TS* __restrict__ h0, TS* __restrict__ ht, const TIO* __restrict__ q,
     const TIO* __restrict__ k, const TIO* __restrict__ v, const float* __restrict__ g,
     const TIO* __restrict__ gx, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, const TIO* __restrict__ beta, TIO* __restrict__ o,
@@ -214,13 +214,20 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   const int64_t sb = ((int64_t)slot * n_heads + h) * (int64_t)(D * D);
 
   // no h0: an empty buffer whose loads read 0 (no branch around the loads)
+  constexpr int ESS = (int)sizeof(TS);
   const __amdgpu_buffer_rsrc_t hr =
-      make_rsrc(const_cast<float*>(h0 ? h0 + sb : h0), h0 ? D * D * 4 : 0);
+      make_rsrc(const_cast<TS*>(h0 ? h0 + sb : h0), h0 ? D * D * ESS : 0);
   f32x4 s[RPT];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         hr, ((rg + RG * i) * D + 4 * cq) * 4, 0, 0));
+  for (int i = 0; i < RPT; ++i) {
+    const int off = ((rg + RG * i) * D + 4 * cq) * ESS;
+    if constexpr (ESS == 4) {
+      s[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(hr, off, 0, 0));
+    } else {
+      const bf16x4 v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(hr, off, 0, 0));
+      s[i] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    }
+  }
 
   // this thread's piece of a block: token rg of the block, elements 4cq..4cq+3
   const float ea = GATE ? __expf(a_log[h]) : 1.f;
@@ -312,27 +319,36 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   }
   if (ht) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<f32x4*>(ht + sb + (rg + RG * i) * D + 4 * cq) = s[i];
+    for (int i = 0; i < RPT; ++i) store_state4(ht + sb + (rg + RG * i) * D + 4 * cq, s[i]);
   }
 }
 
-template <typename TIO, int D>
-static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+template <typename TIO, int D, typename TS>
+static hipError_t launch_recurrent_s(const RecurrentArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
+  const TS* h0 = static_cast<const TS*>(a.h0);
+  TS* ht = static_cast<TS*>(a.ht);
   if (a.gate.mode == GATE_KIMI_)
-    hipLaunchKernelGGL((recurrent_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0,
-                       stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
+    hipLaunchKernelGGL((recurrent_kernel<TIO, D, true, TS>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, h0, ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
                        a.g, (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias,
                        (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
                        a.cu_seqlens, a.slots, a.n_slots, a.qk.kheads, a.qk.norm);
   else
-    hipLaunchKernelGGL((recurrent_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0,
-                       stream, a.h0, a.ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
+    hipLaunchKernelGGL((recurrent_kernel<TIO, D, false, TS>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, h0, ht, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v,
                        a.g, (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
                        (const TIO*)a.beta, (TIO*)a.o, a.scale, a.n_heads, a.t_total,
                        a.cu_seqlens, a.slots, a.n_slots, a.qk.kheads, a.qk.norm);
   return hipGetLastError();
+}
+
+// A bf16 state comes with bf16 inputs only (checked by the C ABI).
+template <typename TIO, int D>
+static hipError_t launch_recurrent_t(const RecurrentArgs& a, hipStream_t stream) {
+  if constexpr (sizeof(TIO) == 2)
+    if (a.state_bf16) return launch_recurrent_s<TIO, D, bf16>(a, stream);
+  return launch_recurrent_s<TIO, D, float>(a, stream);
 }
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
@@ -350,22 +366,30 @@ hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
   }
 }
 
-template <typename TIO, int D>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+template <typename TIO, int D, typename TS>
+static hipError_t launch_decode_s(const DecodeArgs& a, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.n_seqs * a.n_heads;
+  TS* state = static_cast<TS*>(a.state);
   if (a.gate.mode == GATE_KIMI_)
-    hipLaunchKernelGGL((decode_kernel<TIO, D, true>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                       a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
+    hipLaunchKernelGGL((decode_kernel<TIO, D, true, TS>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)a.gate.x, a.gate.a_log, a.gate.dt_bias, a.n_heads,
                        (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots, a.qk.kheads,
                        a.qk.norm);
   else
-    hipLaunchKernelGGL((decode_kernel<TIO, D, false>), dim3((unsigned)nblk), dim3(256), 0, stream,
-                       a.state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
+    hipLaunchKernelGGL((decode_kernel<TIO, D, false, TS>), dim3((unsigned)nblk), dim3(256), 0,
+                       stream, state, (const TIO*)a.q, (const TIO*)a.k, (const TIO*)a.v, a.g,
                        (const TIO*)nullptr, (const float*)nullptr, (const float*)nullptr,
                        a.n_heads, (const TIO*)a.beta, (TIO*)a.o, a.scale, a.slots, a.n_slots,
                        a.qk.kheads, a.qk.norm);
   return hipGetLastError();
+}
+
+template <typename TIO, int D>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (sizeof(TIO) == 2)
+    if (a.state_bf16) return launch_decode_s<TIO, D, bf16>(a, stream);
+  return launch_decode_s<TIO, D, float>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

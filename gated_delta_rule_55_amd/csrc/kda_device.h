@@ -145,6 +145,22 @@ __device__ __forceinline__ float kimi_gate_log2(float z, float ea) {
   return -ea * (zl > 24.f ? zl : __builtin_amdgcn_logf(1.f + fast_exp2(zl)));
 }
 
+// Four consecutive state values (fp32 or bf16 storage) as fp32, and back
+// (bf16 stores round to nearest even).
+__device__ __forceinline__ f32x4 load_state4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ f32x4 load_state4(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void store_state4(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ void store_state4(bf16* p, f32x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
 // Four values of T in one vector (8 bytes for bf16, 16 for fp32).
 template <typename T>
 struct Vec4;

@@ -30,10 +30,11 @@ struct QkArgs {
 
 struct DecodeArgs {
   bool bf16;
+  bool state_bf16 = false;  // the state is stored as bf16 (else fp32)
   int n_seqs, n_heads, d;
   QkArgs qk;
   float scale;
-  float* state;
+  void* state;
   const void *q, *k, *v;
   const float* g;
   const void* beta;
@@ -50,6 +51,7 @@ constexpr int KDA_PLAN_TWO_PASS_ = 2;
 
 struct PrefillArgs {
   bool bf16;
+  bool state_bf16 = false;  // h0 / ht are stored as bf16 (else fp32)
   int n_seqs, n_heads, d, chunk, plan;
   QkArgs qk;
   int64_t t_total;
@@ -57,10 +59,10 @@ struct PrefillArgs {
   const void *q, *k, *v;
   const float* g;
   const void* beta;
-  const float* h0;
+  const void* h0;
   const int32_t* cu_seqlens;  // may be NULL when n_seqs == 1
   void* o;
-  float* ht;
+  void* ht;
   GateArgs gate;
   const int* slots = nullptr;  // h0 / ht pool slot per sequence, or NULL (slot n)
   int n_slots = 0;

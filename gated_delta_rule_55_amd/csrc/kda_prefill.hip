@@ -222,10 +222,10 @@ int scan_tiles(int n_seqs, int n_heads, int cus) {
 }
 template <typename TIO, int D, int C, int NJ>
 __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
-    const float* __restrict__ h0, float* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
+    const void* __restrict__ h0, void* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
     int n_heads, const int* __restrict__ status, const int* __restrict__ chunk_off,
     const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks,
-    const int* __restrict__ slots, int n_slots) {
+    const int* __restrict__ slots, int n_slots, int state_bf16) {
   using Gm = Geo<TIO, D, C>;
   using SS = ScanStep<TIO, D, C, NJ>;
   constexpr int NB = SS::NB;  // column blocks of 16 NJ columns per head
@@ -254,17 +254,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   f32x4 S[NJ][2];
   const size_t sbase = ((size_t)slot * n_heads + h) * D * D;
   // no h0: an empty buffer, whose loads read 0 (branch-free, so the compiler
-  // keeps exact counts of the loads in flight)
-  const __amdgpu_buffer_rsrc_t hr =
-      make_rsrc(const_cast<float*>(h0 ? h0 + sbase : h0), h0 ? D * D * 4 : 0);
+  // keeps exact counts of the loads in flight); a bf16 state is widened
+  const int ess = state_bf16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(
+      const_cast<unsigned char*>(static_cast<const unsigned char*>(h0) + (h0 ? sbase * ess : 0)),
+      h0 ? D * D * ess : 0);
 #pragma unroll
   for (int c = 0; c < NJ; ++c)
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        S[c][m][j] = buffer_load_f32(
-            hr, ((32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16) * 4);
+      for (int j = 0; j < 4; ++j) {
+        const int e = (32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16;
+        const float f32v = buffer_load_f32(hr, state_bf16 ? kBufferOff : e * 4);
+        const float b16v = (float)__builtin_bit_cast(
+            bf16, __builtin_amdgcn_raw_buffer_load_b16(hr, state_bf16 ? e * 2 : kBufferOff, 0, 0));
+        S[c][m][j] = state_bf16 ? b16v : f32v;
+      }
   // Take delivery of h0 here, before the operator loads are issued: S then
   // enters the loop with nothing in flight, and the loop's own waits are
   // counted exactly (an empty asm that reads and writes S; emits nothing).
@@ -322,9 +328,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          ht[sbase + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16] =
-              S[c][m][j];
+        for (int j = 0; j < 4; ++j) {
+          const size_t e =
+              sbase + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * (NJ * jb + c) + l16;
+          if (state_bf16) static_cast<bf16*>(ht)[e] = (bf16)S[c][m][j];
+          else static_cast<float*>(ht)[e] = S[c][m][j];
+        }
   }
 }
 
@@ -564,7 +573,7 @@ hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk
   const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * SS::NB);
   hipLaunchKernelGGL((state_scan_kernel<TIO, D, C, NJ>), dim3(nblk), dim3(64 * (D / 32)),
                      SS::LDS_BYTES, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
-                     chunk_off, tab, blocks, a.slots, a.n_slots);
+                     chunk_off, tab, blocks, a.slots, a.n_slots, (int)a.state_bf16);
   return hipGetLastError();
 }
 
@@ -629,8 +638,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
       fa.v = a.v;
       fa.g = a.g;
       fa.beta = a.beta;
-      fa.h0 = a.h0;
-      fa.ht = a.ht;
+      fa.h0 = static_cast<const float*>(a.h0);  // fp32 states only on this plan
+      fa.ht = static_cast<float*>(a.ht);
       fa.o = a.o;
       fa.n_seqs = a.n_seqs;
       fa.n_heads = a.n_heads;

@@ -66,6 +66,7 @@ def _check_gate(gate, g, lead, H, dk, dtype, dev):
 def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=64, o=None,
                  ht=None, plan="auto", gate=None, state_indices=None,
                  n_slots=0, qk_l2norm=False) -> _abi.PrefillDesc:
+    st = h0 if h0 is not None else ht
     T, Hg, dk = q.shape
     H, dv = v.shape[1], v.shape[-1]
     N = 1 if cu_seqlens is None else int(cu_seqlens.shape[0]) - 1
@@ -74,11 +75,24 @@ def prefill_desc(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None, chunk=6
         plan=_PLANS[plan], t_total=T, scale=0.0 if scale is None else float(scale), q=_ptr(q), k=_ptr(k),
         v=_ptr(v), g=_ptr(g), beta=_ptr(beta), h0=_ptr(h0), cu_seqlens=_ptr(cu_seqlens),
         o=_ptr(o), ht=_ptr(ht), gate=_gate_tuple(gate), state_indices=_ptr(state_indices),
-        n_slots=int(n_slots), n_k_heads=Hg, qk_l2norm=int(bool(qk_l2norm)))
+        n_slots=int(n_slots), n_k_heads=Hg, qk_l2norm=int(bool(qk_l2norm)),
+        state_dtype=_DTYPES[st.dtype] if st is not None else _abi.KDA_DTYPE_F32)
+
+
+def _state_dtype(h0, ht, state_dtype):
+    """dtype of the states of one call: that of h0 or ht when given (they must
+    agree), else `state_dtype` (fp32 by default) for a newly allocated ht."""
+    given = [t.dtype for t in (h0, ht) if t is not None]
+    sd = given[0] if given else (state_dtype or torch.float32)
+    if sd not in _DTYPES or any(x != sd for x in given):
+        raise TypeError(f"states must share one dtype of fp32/bf16, got {given or [sd]}")
+    if state_dtype is not None and state_dtype != sd:
+        raise TypeError(f"state_dtype {state_dtype} but the states are {sd}")
+    return sd
 
 
 def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht, output_final_state, gate,
-                  state_indices, state_pool_slots):
+                  state_indices, state_dtype):
     """Shared checks of the prefill entry points; returns (N, n_slots, out, ht)."""
     dev = q.device
     if dev.type != "cuda":
@@ -106,17 +120,18 @@ def _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht, output_final_state,
         if pool is None:
             raise ValueError("state_indices needs a state pool (h0 and/or ht)")
         S = int(pool.shape[0])
+    sd = _state_dtype(h0, ht, state_dtype)
     if h0 is not None:
-        _check(h0, "h0", (S, H, dk, dv), torch.float32, dev)
+        _check(h0, "h0", (S, H, dk, dv), sd, dev)
     if out is None:
         out = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     else:
         _check(out, "out", (T, H, dv), q.dtype, dev)
     if ht is None and output_final_state:
-        ht = h0 if state_indices is not None else torch.empty((N, H, dk, dv), dtype=torch.float32,
+        ht = h0 if state_indices is not None else torch.empty((N, H, dk, dv), dtype=sd,
                                                                 device=dev)
     if ht is not None:
-        _check(ht, "ht", (S, H, dk, dv), torch.float32, dev)
+        _check(ht, "ht", (S, H, dk, dv), sd, dev)
     return N, (S if state_indices is not None else 0), out, ht
 
 
@@ -134,7 +149,8 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   ht: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   output_final_state: bool = True, stream=None, events=None,
                   plan: str = "auto", gate=None,
-                  state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False
+                  state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                  state_dtype: Optional[torch.dtype] = None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k: [T, Hg, dk] (Hg key heads, each shared by
     H / Hg consecutive value heads; Hg = H by default); g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
@@ -150,10 +166,13 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     (g may then be None).  `state_indices` (int32 [N] on the device): h0 and
     ht are then state pools [S, H, dk, dv] (ht defaults to h0: in place) and
     sequence n uses slot state_indices[n]; a negative slot skips it.
-    `qk_l2norm`: L2-normalise every q and k row in the kernels (eps 1e-6)."""
+    `qk_l2norm`: L2-normalise every q and k row in the kernels (eps 1e-6).
+    States (h0, ht) are fp32, or bf16 with bf16 inputs: their dtype is that of
+    h0 / ht when given, else `state_dtype` (fp32 by default) for a new ht.  The
+    arithmetic is fp32 either way; a bf16 ht is rounded once when written."""
     dev = q.device
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
-                                        output_final_state, gate, state_indices, None)
+                                        output_final_state, gate, state_indices, state_dtype)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate,
                         state_indices, n_slots, qk_l2norm)
     need = _abi.workspace_bytes(desc)
@@ -181,13 +200,14 @@ def recurrent_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                       cu_seqlens: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                       out: Optional[torch.Tensor] = None, ht: Optional[torch.Tensor] = None,
                       output_final_state: bool = True, stream=None, gate=None,
-                      state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False
+                      state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                      state_dtype: Optional[torch.dtype] = None
                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """The prefill of chunk_prefill computed token by token with the state held
     on chip (for continuing prefills of a few tokens on a carried state).  Same
     arguments and results; no chunk, plan or workspace."""
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
-                                        output_final_state, gate, state_indices, None)
+                                        output_final_state, gate, state_indices, state_dtype)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, 64, out, ht, "auto", gate,
                         state_indices, n_slots, qk_l2norm)
     st = _abi.recurrent_prefill_raw(desc, _stream(stream))
@@ -201,7 +221,9 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
                      out: Optional[torch.Tensor] = None, stream=None, gate=None,
                      state_indices: Optional[torch.Tensor] = None,
                      qk_l2norm: bool = False) -> torch.Tensor:
-    """One recurrent decode step; `state` [N, H, dk, dv] fp32 is updated in place.
+    """One recurrent decode step; `state` [N, H, dk, dv] is updated in place.
+    The state is fp32, or bf16 with bf16 inputs (fp32 arithmetic, rounded once
+    when written back).
     q, k: [N, Hg, dk] (Hg divides H); g: [N, H, dk]; v: [N, H, dv]; beta: [N, H].
     Returns o [N, H, dv].  `qk_l2norm` as in chunk_prefill.
     `gate` as in chunk_prefill (x is [N, H, dk]).  `state_indices` (int32 [N]
@@ -215,7 +237,9 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
         raise TypeError(f"unsupported dtype {q.dtype}")
     S, H, dk, dv = state.shape
     N = S if state_indices is None else int(q.shape[0])
-    _check(state, "state", (S, H, dk, dv), torch.float32, dev)
+    if state.dtype not in _DTYPES:
+        raise TypeError(f"state must be fp32 or bf16, got {state.dtype}")
+    _check(state, "state", (S, H, dk, dv), state.dtype, dev)
     if state_indices is not None:
         _check(state_indices, "state_indices", (N,), torch.int32, dev)
     Hg = int(q.shape[1]) if q.dim() == 3 else H
@@ -236,7 +260,7 @@ def recurrent_decode(state: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: t
                             beta=beta.data_ptr(), o=out.data_ptr(), gate=_gate_tuple(gate),
                             state_indices=_ptr(state_indices),
                             n_slots=S if state_indices is not None else 0, n_k_heads=Hg,
-                            qk_l2norm=int(bool(qk_l2norm)))
+                            qk_l2norm=int(bool(qk_l2norm)), state_dtype=_DTYPES[state.dtype])
     st = _abi.recurrent_decode_raw(desc, _stream(stream))
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_recurrent_decode")

@@ -40,7 +40,12 @@
  *     index tables), its element size.
  *   - Supported: dk = dv = d in {32, 64, 128}; chunk in {16, 32, 64};
  *     dtype KDA_DTYPE_F32 or KDA_DTYPE_BF16 for q, k, v, beta and o.
- *     g, h0, ht and the decode state are always fp32.
+ *     g is fp32.  h0, ht and the decode state are fp32, or bf16 when
+ *     state_dtype asks for it (bf16 inputs only): the state dtype is a
+ *     property of the state pool (page "model(kimi_linear): ONE-SURFACE ROW
+ *     7", B3: the conv cache dtype mirrors kda_state_dtype).  The
+ *     arithmetic stays fp32; a bf16 state is rounded (to nearest even) once
+ *     per call when it is written.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -52,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -143,10 +148,10 @@ typedef struct {
   const void* v;
   const float* g;
   const void* beta;
-  const float* h0;            /* NULL = zero initial state                      */
+  const void* h0;             /* NULL = zero initial state; state_dtype         */
   const int32_t* cu_seqlens;  /* NULL allowed when n_seqs == 1                  */
   void* o;
-  float* ht;                  /* NULL = final state not returned               */
+  void* ht;                   /* NULL = final state not returned; state_dtype  */
   kda_gate_desc gate;         /* g, or the raw gate and its parameters; g may  */
                               /* be NULL when gate.mode = KIMI                 */
   const int32_t* state_indices; /* NULL, or device [N]: h0 and ht are state    */
@@ -158,6 +163,7 @@ typedef struct {
   int32_t n_slots;            /* pool size when state_indices is set           */
   int32_t n_k_heads;          /* Hg, dividing H; 0 = H                         */
   int32_t qk_l2norm;          /* 1 = L2-normalise q and k rows in the kernels  */
+  int32_t state_dtype;        /* kda_dtype of h0 and ht; 0 = fp32              */
 } kda_prefill_desc;
 
 /* One recurrent decode step for a batch of N sequences, one token each.
@@ -171,7 +177,7 @@ typedef struct {
   int32_t n_heads;            /* H >= 1                                         */
   int32_t dk, dv;             /* dk == dv in {32, 64, 128}                      */
   float scale;                /* 0 = dk^-1/2                                    */
-  float* state;
+  void* state;                /* state_dtype (fp32 unless asked for bf16)       */
   const void* q;
   const void* k;
   const void* v;
@@ -186,6 +192,7 @@ typedef struct {
   int32_t n_slots;            /* pool size when state_indices is set           */
   int32_t n_k_heads;          /* Hg, dividing H; 0 = H                         */
   int32_t qk_l2norm;          /* 1 = L2-normalise q and k in the kernel        */
+  int32_t state_dtype;        /* kda_dtype of the state; 0 = fp32              */
 } kda_decode_desc;
 
 /* Recurrent prefill: the same computation as kda_chunk_prefill (same

@@ -276,3 +276,33 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_abi, "LIB_PATH", "/nonexistent/libkda.so")
     with pytest.raises(RuntimeError, match="missing"):
         _abi.lib()
+
+
+@no_gpu_only
+def test_state_dtype_validation(abi):
+    """The state dtype is fp32 (0 or KDA_DTYPE_F32) or bf16 with bf16 inputs;
+    byte ranges of bf16 states are half as long."""
+    F32, BF16 = abi.KDA_DTYPE_F32, abi.KDA_DTYPE_BF16
+    ws = (0x10000000, 1 << 30, 0)
+    assert abi.chunk_prefill_raw(_valid_prefill(abi, state_dtype=7), *ws) == abi.KDA_ERR_DTYPE
+    d = _valid_prefill(abi, dtype=F32, state_dtype=BF16)
+    assert abi.chunk_prefill_raw(d, *ws) == abi.KDA_ERR_UNSUPPORTED
+    assert abi.recurrent_prefill_raw(d, 0) == abi.KDA_ERR_UNSUPPORTED
+    # 1 x 2 x 128 x 128 states: 64 KiB in bf16, 128 KiB in fp32
+    h0 = 0x700000
+    d = _valid_prefill(abi, h0=h0, ht=h0 + 65536, state_dtype=F32)
+    assert abi.chunk_prefill_raw(d, *ws) == abi.KDA_ERR_ALIAS
+    d = _valid_prefill(abi, h0=h0, ht=h0 + 65536, state_dtype=BF16)
+    assert abi.chunk_prefill_raw(d, *ws) == abi.KDA_ERR_HIP      # checks pass; no device
+    kw = dict(dtype=BF16, n_seqs=2, n_heads=2, dk=64, dv=64, state=0x100000, q=0x900000,
+              k=0xa00000, v=0xb00000, g=0xc00000, beta=0xd00000, o=0xe00000)
+    assert abi.recurrent_decode_raw(abi.decode_desc(**kw, state_dtype=5), 0) == abi.KDA_ERR_DTYPE
+    assert abi.recurrent_decode_raw(abi.decode_desc(**dict(kw, dtype=F32), state_dtype=BF16),
+                                    0) == abi.KDA_ERR_UNSUPPORTED
+    # a pool of 40 bf16 slots spans 40 x 2 x 64 x 64 x 2 bytes: o just past it
+    o = 0x100000 + 40 * 2 * 64 * 64 * 2 + 64
+    pool = dict(state_indices=0xf00000, n_slots=40)
+    assert abi.recurrent_decode_raw(abi.decode_desc(**dict(kw, o=o), **pool, state_dtype=F32),
+                                    0) == abi.KDA_ERR_ALIAS
+    assert abi.recurrent_decode_raw(abi.decode_desc(**dict(kw, o=o), **pool, state_dtype=BF16),
+                                    0) == abi.KDA_ERR_HIP
