@@ -34,6 +34,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 # The CPU oracle (OpenMP) runs last; its idle threads sleep instead of
@@ -106,18 +108,20 @@ def bench_prefill(args, torch, kda, synth, inp=None, fused_gate=False):
         log("generating the prefill-32k inputs (seeded numpy)")
         inp = synth.make_config(2)
     T, H, D = inp.T, inp.H, inp.dk
+    N = len(inp.cu_seqlens) - 1
     q, k, v = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v))
     beta = to_dev(inp.beta, torch)
+    cu = None if N == 1 else torch.from_numpy(inp.cu_seqlens).cuda()
     if fused_gate:
         g = None
         gate = (to_dev(inp.gate_x, torch), to_dev(inp.gate_a_log, torch),
                 to_dev(inp.gate_dt_bias, torch))
     else:
         g, gate = to_dev(inp.g, torch), None
-    h0 = to_dev(inp.h0, torch)
+    h0 = None if inp.h0 is None else to_dev(inp.h0, torch)
     o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
-    ht = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kda.prefill_workspace_bytes(T, H, D, 1, 64), dtype=torch.uint8, device="cuda")
+    ht = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.prefill_workspace_bytes(T, H, D, N, 64), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in ev:  # create the underlying events
@@ -126,7 +130,7 @@ def bench_prefill(args, torch, kda, synth, inp=None, fused_gate=False):
     torch.cuda.synchronize()
 
     def run(events=None):
-        kda.chunk_prefill(q, k, v, g, beta, h0, None, scale=inp.scale, chunk=64, out=o, ht=ht,
+        kda.chunk_prefill(q, k, v, g, beta, h0, cu, scale=inp.scale, chunk=64, out=o, ht=ht,
                           workspace=ws, events=events, plan=args.plan, gate=gate)
 
     for _ in range(args.warmup):
@@ -154,9 +158,36 @@ def bench_prefill(args, torch, kda, synth, inp=None, fused_gate=False):
     return inp, ms_per_step, avg
 
 
-def bench_decode(args, torch, kda, synth):
-    log("generating the decode-64x256 inputs (seeded numpy)")
-    inp = synth.make_config(4)
+def bench_prefill_batch(args, torch, kda, synth, cfg, full=None):
+    """Batched prefills: the packed varlen batch (8 sequences, lengths in
+    [300, 8192], h0 given) and the 64 x 1024-token prefill that seeds the
+    decode leg (no h0).  Wider scan blocks apply here (many sequence-heads)."""
+    if cfg == 3:
+        log("generating the varlen-8 prefill inputs (seeded numpy)")
+        inp = synth.make_config(3)
+        name = "varlen-8: 8 packed sequences, lengths seeded in [300, 8192]"
+    else:
+        N, L, P = 64, 1280, 1024
+        rows = np.concatenate([np.arange(n * L, n * L + P) for n in range(N)])
+        inp = synth.KdaInputs(**{**full.__dict__, **{
+            f: getattr(full, f)[rows] for f in ("q", "k", "v", "g", "beta", "gate_x")
+            if getattr(full, f) is not None},
+            "cu_seqlens": np.arange(0, N * P + 1, P, dtype=np.int32)})
+        name = "64 x 1024: the prefill that seeds the decode leg"
+    _, ms_step, stage = bench_prefill(args, torch, kda, synth, inp=inp)
+    T, N = inp.T, len(inp.cu_seqlens) - 1
+    nstate = N * (2 if inp.h0 is not None else 1)
+    alg = T * BYTES_PER_TOKEN + nstate * STATE_BYTES
+    ach = alg / (stage["prefill_call"] / 1e3) / 1e9
+    return {"workload": name + f", {T} tokens, H=32, d=128, chunk 64, bf16",
+            "tokens_per_s": round(T / (ms_step / 1e3), 1), "ms_per_step": round(ms_step, 4),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                         "scope": f"whole prefill pass, {alg} algorithmic bytes per pass"},
+            "kernels_ms": {kname: round(v, 4) for kname, v in stage.items()}}
+
+
+def bench_decode(args, torch, kda, synth, inp):
     N, L, P, S = 64, 1280, 1024, args.decode_steps
     H, D = inp.H, inp.dk
     dev = {name: to_dev(getattr(inp, name), torch) for name in ["q", "k", "v", "g", "beta"]}
@@ -167,31 +198,45 @@ def bench_decode(args, torch, kda, synth):
     cu = torch.arange(0, N * P + 1, P, dtype=torch.int32, device="cuda")
     _, state0 = kda.chunk_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, cu,
                                   scale=inp.scale, chunk=64)
-    state = state0.clone()
     out = torch.empty((S, N, H, D), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    eager, ms = _decode_steps_timed(args, torch, kda, inp, state0, dec, out, stream)
+    # the same steps on a bf16 copy of the state (half the state bytes)
+    eager16, ms16 = _decode_steps_timed(args, torch, kda, inp, state0.to(torch.bfloat16), dec,
+                                        out, stream)
+    rec = bench_recurrent(args, torch, kda, inp, state0, dec, stream)
+    rec["eager_decode_ms_per_step"] = round(eager / S, 5)
+    rec["bf16_state"] = {"ms": ms16, "eager_ms_per_step": round(eager16 / S, 5)}
+    return inp, S, ms, dec, rec
+
+
+def _decode_steps_timed(args, torch, kda, inp, state0, dec, out, stream):
+    """S decode steps from state0: median eager time (one Python call per
+    step) and median time of the same steps replayed from a captured graph,
+    as a serving loop issues decode (the kernels' own time, without per-call
+    host cost).  Each replay is checked bit for bit against the eager run."""
+    S = out.shape[0]
+    state = state0.clone()
 
     def steps():
         for s in range(S):
             kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
                                  dec["beta"][s], scale=inp.scale, out=out[s])
 
-    state.copy_(state0)
-    steps()  # warm-up
-    eager = []
-    for _ in range(args.decode_reps):
+    def timed(fn):
         state.copy_(state0)  # restore, untimed
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        steps()  # issued from Python, one call per step
+        fn()
         b.record(stream)
         torch.cuda.synchronize()
-        eager.append(a.elapsed_time(b))
+        return a.elapsed_time(b)
+
+    state.copy_(state0)
+    steps()  # warm-up
+    eager = [timed(steps) for _ in range(args.decode_reps)]
     out_ref, state_ref = out.clone(), state.clone()
-    # The S steps captured once in a graph and replayed, as a serving loop
-    # issues decode: the kernels' own time, without per-call host cost.  Each
-    # replay is checked bit for bit against the eager run.
     graph = torch.cuda.CUDAGraph()
     state.copy_(state0)
     torch.cuda.synchronize()
@@ -201,20 +246,10 @@ def bench_decode(args, torch, kda, synth):
             steps()
     times = []
     for _ in range(max(3, args.decode_reps)):
-        state.copy_(state0)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        graph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
+        times.append(timed(graph.replay))
         if not (torch.equal(state, state_ref) and torch.equal(out, out_ref)):
             raise RuntimeError("graph replay of the decode steps differs from the eager run")
-    ms = statistics.median(times)
-    rec = bench_recurrent(args, torch, kda, inp, state0, dec, stream)
-    rec["eager_decode_ms_per_step"] = round(statistics.median(eager) / S, 5)
-    return inp, S, ms, dec, rec
+    return statistics.median(eager), statistics.median(times)
 
 
 def bench_recurrent(args, torch, kda, inp, state0, dec, stream, R=16):
@@ -417,6 +452,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg")
+    ap.add_argument("--no-batch", action="store_true",
+                    help="skip the batched prefill legs (varlen-8, 64 x 1024)")
     ap.add_argument("--no-gate", action="store_true", help="skip the fused-gate prefill leg")
     ap.add_argument("--no-conv", action="store_true", help="skip the causal conv leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -485,8 +522,15 @@ def main():
                          "scope": f"whole prefill pass, {gbytes} algorithmic bytes per pass"},
             "kernels_ms": {kname: round(v, 4) for kname, v in gstage.items()},
         }
+    inp4 = None
+    if not (args.no_batch and args.no_decode):
+        log("generating the decode-64x256 inputs (seeded numpy)")
+        inp4 = synth.make_config(4)
+    if not args.no_batch:
+        line["prefill_batches"] = [bench_prefill_batch(args, torch, kda, synth, 3),
+                                   bench_prefill_batch(args, torch, kda, synth, 4, inp4)]
     if not args.no_decode:
-        dinp, S, dms, dec, rec = bench_decode(args, torch, kda, synth)
+        dinp, S, dms, dec, rec = bench_decode(args, torch, kda, synth, inp4)
         step_ms = dms / S
         dbytes = DECODE_STATE_BYTES + DECODE_TOKEN_BYTES
         dach = dbytes / (step_ms / 1e3) / 1e9
@@ -501,6 +545,22 @@ def main():
                          "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode"),
                          "note": "the 134 MB state fits the 256 MB Infinity Cache"},
+        }
+        b16 = rec.pop("bf16_state")
+        step16 = b16["ms"] / S
+        bytes16 = DECODE_STATE_BYTES // 2 + DECODE_TOKEN_BYTES
+        ach16 = bytes16 / (step16 / 1e3) / 1e9
+        line["decode_bf16_state"] = {
+            "workload": "decode-64x256 as above with the state held in bf16 (fp32 arithmetic, "
+                        "state rounded once per step when written)",
+            "steps_per_s": round(1e3 / step16, 1), "ms_per_step": round(step16, 5),
+            "eager_ms_per_step": b16["eager_ms_per_step"],
+            "tokens_per_s": round(64 * 1e3 / step16, 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach16, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(ach16 / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_bf16_state"),
+                         "scope": f"bf16 state read + write once and the step's inputs and "
+                                  f"outputs, {bytes16} bytes per step"},
         }
         line["recurrent_prefill"] = rec
     if not args.no_conv:
