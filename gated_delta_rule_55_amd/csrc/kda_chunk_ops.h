@@ -390,10 +390,12 @@ struct ChunkLocal {
     const int l16 = lane & 15;
     const int lg = lane >> 4;
     const TIO zero_t = from_f32<TIO>(0.f);
-    // (8 rows x 1 channel) groups of the elementwise passes: lanes run along
-    // channels, so scalar LDS accesses of a row are conflict-free and the
-    // eight tokens of a group leave as one 16-byte transposed store.
-    constexpr int NGRP = (C / 8) * D / NT > 0 ? (C / 8) * D / NT : 1;
+    // (8 rows x 2 channels) groups of the elementwise passes: lanes run along
+    // channel pairs, so every LDS access of a row is one conflict-free 2-value
+    // word, and each channel's eight tokens leave as one 16-byte transposed
+    // store.
+    using V2 = typename Vec2<TIO>::type;
+    constexpr int NGRP = (C / 8) * (D / 2) / NT > 0 ? (C / 8) * (D / 2) / NT : 1;
 
     // ---- phase 0: stage k, q, v, g (base 2) and beta; clear padding --------
     // rows at or past the chunk's length are staged as zeros (bit masks, so
@@ -485,13 +487,17 @@ struct ChunkLocal {
 #pragma unroll
     for (int m = 0; m < NGRP; ++m) {
       const int grp = tid + NT * m;
-      const int c = grp % D, r0 = 8 * (grp / D);
+      const int c = 2 * (grp % (D / 2)), r0 = 8 * (grp / (D / 2));
       if (r0 < C) {
-        typename Frag<TIO>::type vb;
+        FragT vb0, vb1;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vb[e] = from_f32<TIO>(s_beta[r0 + e] * to_f32(Vs[(r0 + e) * KS_LD + c]));
-        store_frag8(VBt + c * TK_LD + r0, vb);
+        for (int e = 0; e < 8; ++e) {
+          const V2 vv = *reinterpret_cast<const V2*>(Vs + (r0 + e) * KS_LD + c);
+          vb0[e] = from_f32<TIO>(s_beta[r0 + e] * to_f32(vv[0]));
+          vb1[e] = from_f32<TIO>(s_beta[r0 + e] * to_f32(vv[1]));
+        }
+        store_frag8(VBt + c * TK_LD + r0, vb0);
+        store_frag8(VBt + (c + 1) * TK_LD + r0, vb1);
       }
     }
     __syncthreads();
@@ -501,27 +507,36 @@ struct ChunkLocal {
 #pragma unroll
     for (int m = 0; m < NGRP; ++m) {
       const int grp = tid + NT * m;
-      const int c = grp % D, r0 = 8 * (grp / D);
+      const int c = 2 * (grp % (D / 2)), r0 = 8 * (grp / (D / 2));
       if (r0 < C) {
         const int a = r0 >> 4;
-        const float ra = rho[a * D + c], rb = rho[(a + 1) * D + c];
-        const float sa = fast_exp2(ra);
-        typename Frag<TIO>::type kb;
+        const f32x2 ra = *reinterpret_cast<const f32x2*>(rho + a * D + c);
+        const f32x2 rb = *reinterpret_cast<const f32x2*>(rho + (a + 1) * D + c);
+        const float sa[2] = {fast_exp2(ra[0]), fast_exp2(ra[1])};
+        FragT kb[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = r0 + e;
-          const float G = Gs[r * GS_LD + c];
-          const float el = fast_exp2(G - ra);
-          const float er = fast_exp2(rb - G);
-          const float kv = to_f32(Lk[r * KS_LD + c]);
-          const float qv = to_f32(Lq[r * KS_LD + c]);
-          const float lk = kv * el;
-          Lk[r * KS_LD + c] = from_f32<TIO>(lk);
-          Lq[r * KS_LD + c] = from_f32<TIO>(qv * el);
-          Rn[r * KS_LD + c] = from_f32<TIO>(kv * er);
-          kb[e] = from_f32<TIO>(s_beta[r] * lk * sa);
+          const f32x2 G = *reinterpret_cast<const f32x2*>(Gs + r * GS_LD + c);
+          const V2 kv = *reinterpret_cast<const V2*>(Lk + r * KS_LD + c);
+          const V2 qv = *reinterpret_cast<const V2*>(Lq + r * KS_LD + c);
+          V2 lk2, lq2, rn2;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const float el = fast_exp2(G[i] - ra[i]);
+            const float er = fast_exp2(rb[i] - G[i]);
+            const float lk = to_f32(kv[i]) * el;
+            lk2[i] = from_f32<TIO>(lk);
+            lq2[i] = from_f32<TIO>(to_f32(qv[i]) * el);
+            rn2[i] = from_f32<TIO>(to_f32(kv[i]) * er);
+            kb[i][e] = from_f32<TIO>(s_beta[r] * lk * sa[i]);
+          }
+          *reinterpret_cast<V2*>(Lk + r * KS_LD + c) = lk2;
+          *reinterpret_cast<V2*>(Lq + r * KS_LD + c) = lq2;
+          *reinterpret_cast<V2*>(Rn + r * KS_LD + c) = rn2;
         }
-        store_frag8(KBt + c * TK_LD + r0, kb);
+        store_frag8(KBt + c * TK_LD + r0, kb[0]);
+        store_frag8(KBt + (c + 1) * TK_LD + r0, kb[1]);
       }
     }
     for (int c = tid; c < D; c += NT) {
@@ -583,27 +598,6 @@ struct ChunkLocal {
           Aq[rr * TK_LD + ii] = from_f32<TIO>((ii <= rr) ? aqk[j] : 0.f);
         }
       }
-      // Kg^T fragments in kperm token order: element (kt, ts, lane, e) =
-      // Kg[32ts + kperm(lg, e)][16kt + l16], Kg = Rn * 2^(rho_TT - rho_{blk+1}).
-      for (int slot = tid; slot < DT * KBC * 64; slot += NT) {
-        const int ln = slot & 63;
-        const int kt = (slot >> 6) / KBC, ts = (slot >> 6) % KBC;
-        const int c = 16 * kt + (ln & 15);
-        const int g4 = ln >> 4;
-        FragT f;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int blk = 2 * ts + hh;  // 16-token block of these four tokens
-          const float fk = (blk < TT) ? fac[fac_kg(blk < TT ? blk : 0) * D + c] : 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = 16 * blk + 4 * g4 + e;
-            f[4 * hh + e] = from_f32<TIO>((blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fk : 0.f);
-          }
-        }
-        store_frag8(out.k + (size_t)slot * 8, f);
-      }
-      for (int c = tid; c < D; c += NT) out.gam[c] = fast_exp2(rho[TT * D + c]);
     }
     __syncthreads();
 
@@ -612,7 +606,7 @@ struct ChunkLocal {
     // column-oriented substitution, row i of the inverse reaching the rows
     // below it by a row broadcast; then the off-diagonal blocks one band at
     // a time, one wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
-    // (fp32 MFMA).
+    // (fp32 MFMA).  Meanwhile the other waves write the Kg^T fragments and Gam.
     if (wave == 0) {
       const int a = lg < TT ? lg : TT - 1;  // rows past the blocks: a copy, unused
       const int r = l16;
@@ -643,6 +637,28 @@ struct ChunkLocal {
 #pragma unroll
         for (int j = 0; j < 16; ++j) brow[j] = from_f32<TIO>(X[j]);
       }
+    } else {
+      // Kg^T fragments in kperm token order: element (kt, ts, lane, e) =
+      // Kg[32ts + kperm(lg, e)][16kt + l16], Kg = Rn * 2^(rho_TT - rho_{blk+1}).
+      for (int slot = tid - 64; slot < DT * KBC * 64; slot += NT - 64) {
+        const int ln = slot & 63;
+        const int kt = (slot >> 6) / KBC, ts = (slot >> 6) % KBC;
+        const int c = 16 * kt + (ln & 15);
+        const int g4 = ln >> 4;
+        FragT f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int blk = 2 * ts + hh;  // 16-token block of these four tokens
+          const float fk = (blk < TT) ? fac[fac_kg(blk < TT ? blk : 0) * D + c] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = 16 * blk + 4 * g4 + e;
+            f[4 * hh + e] = from_f32<TIO>((blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fk : 0.f);
+          }
+        }
+        store_frag8(out.k + (size_t)slot * 8, f);
+      }
+      for (int c = tid - 64; c < D; c += NT - 64) out.gam[c] = fast_exp2(rho[TT * D + c]);
     }
     __syncthreads();
 #pragma unroll

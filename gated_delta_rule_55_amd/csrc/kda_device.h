@@ -161,6 +161,20 @@ __device__ __forceinline__ void store_state4(bf16* p, f32x4 v) {
   *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
+// Two values of T in one vector (4 bytes for bf16, 8 for fp32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+struct Vec2;
+template <>
+struct Vec2<bf16> {
+  typedef bf16x2 type;
+};
+template <>
+struct Vec2<float> {
+  typedef f32x2 type;
+};
+
 // Four values of T in one vector (8 bytes for bf16, 16 for fp32).
 template <typename T>
 struct Vec4;
