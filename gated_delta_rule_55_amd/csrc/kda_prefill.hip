@@ -140,18 +140,25 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
     for (int n = tid; n < n_seqs; n += 256) chunk_off[n] = 0;
     return;
   }
-  for (int n = tid; n < n_seqs; n += 256) {
-    const int64_t s = cu_at(n), e = cu_at(n + 1);
-    const int first = chunk_off[n];
-    int j = 0;
-    for (int64_t p = s; p < e; p += chunk, ++j) {
-      ChunkEnt ent;
-      ent.seq = n;
-      ent.start = (int)p;
-      ent.len = (int)((e - p) < chunk ? (e - p) : chunk);
-      ent.idx = j;
-      tab[first + j] = ent;
+  // One table entry per thread: chunk i belongs to the last sequence whose
+  // first chunk is <= i (empty sequences own no chunk, so the search never
+  // stops on one).  A single long sequence fills its table in parallel.
+  const int total = s_carry;
+  for (int i = tid; i < total; i += 256) {
+    int lo = 0, hi = n_seqs;  // chunk_off[lo] <= i < chunk_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (chunk_off[mid] <= i) lo = mid;
+      else hi = mid;
     }
+    const int j = i - chunk_off[lo];
+    const int64_t p = cu_at(lo) + (int64_t)j * chunk, e = cu_at(lo + 1);
+    ChunkEnt ent;
+    ent.seq = lo;
+    ent.start = (int)p;
+    ent.len = (int)((e - p) < chunk ? (e - p) : chunk);
+    ent.idx = j;
+    tab[i] = ent;
   }
 }
 
@@ -303,10 +310,17 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     buf.start = tab[ci].start;
     buf.len = tab[ci].len;
   };
+  // The three fetches stay in this order (scheduling barriers): the wait
+  // counts at the loop head are merged over this prologue and the loop's
+  // back edge, so a load of the first buffer that the scheduler sank below
+  // the others would make every step wait on recent loads.
   if (c_begin < c_end) {
     fetch(b0, c_begin + 0);
+    __builtin_amdgcn_sched_barrier(0);
     fetch(b1, c_begin + 1);
+    __builtin_amdgcn_sched_barrier(0);
     fetch(b2, c_begin + 2);
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
   // The loop body runs its three steps unconditionally (a step past the last
