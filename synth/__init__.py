@@ -11,6 +11,7 @@ from .kda_inputs import (  # noqa: F401
     f64_to_bf16_bits,
     make_config,
     make_inputs,
+    seeded_lengths,
     slice_heads,
 )
 from .conv_inputs import ConvInputs, make_conv_inputs, seeded_conv_lengths  # noqa: F401

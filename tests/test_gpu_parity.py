@@ -143,3 +143,28 @@ def test_bad_cu_seqlens_reported(kda):
     good = d["cu_seqlens"]
     kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, good, out=o, workspace=ws)
     assert kda.workspace_status(ws) == 0
+
+
+@pytest.mark.parametrize("dtype,d,chunk,n,hi", [
+    ("f32", 32, 16, 600, 40),     # more than 256 sequences: several passes of the offset scan
+    ("bf16", 128, 64, 300, 150),  # the workload head shape, many partial chunks
+])
+def test_many_short_sequences(kda, dtype, d, chunk, n, hi):
+    """Hundreds of packed sequences, about a tenth of them empty: every chunk's
+    table entry (its sequence found by search over the chunk offsets) must
+    send it to the right sequence, so o and every final state match the
+    oracle run sequence by sequence."""
+    lengths = synth.seeded_lengths(17 + n, n, 0, hi)
+    lengths = [0 if i % 10 == 3 else L for i, L in enumerate(lengths)]
+    say(f"prefill {n} sequences dtype={dtype} d={d} C={chunk} tokens={sum(lengths)}")
+    inp = synth.make_inputs(19, lengths, 2, d, dtype=dtype,
+                            gate="softplus" if dtype == "f32" else "kimi", h0_std=0.05,
+                            chunk=chunk)
+    o, hT = run_prefill(kda, inp)
+    o_ref, hT_ref = oracle_prefill(inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(hT, hT_ref)
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    # empty sequences carry h0 through unchanged
+    empty = [i for i, L in enumerate(lengths) if L == 0]
+    assert np.array_equal(hT[empty], inp.h0[empty].astype(np.float64))
