@@ -109,6 +109,13 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
     if (!kda::prefill_supported(d->dtype == KDA_DTYPE_BF16, d->dk, chunk))
       return KDA_ERR_UNSUPPORTED;
   }
+  // Workgroup and item counts stay in 32-bit range: the scan runs up to
+  // n_seqs x n_heads x (dk / 16) workgroups, the recurrent prefill
+  // n_seqs x n_heads, and the chunk-local stage walks up to
+  // (t_total / chunk + n_seqs) x n_heads (chunk, head) items.
+  if ((int64_t)d->n_seqs * d->n_heads * (d->dk / 16) > INT32_MAX) return KDA_ERR_SHAPE;
+  if (chunked && ((int64_t)d->t_total / chunk + d->n_seqs) * d->n_heads > INT32_MAX)
+    return KDA_ERR_SHAPE;
   if (!(std::isfinite(d->scale))) return KDA_ERR_SHAPE;
   if (chunked &&
       d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)

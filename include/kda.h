@@ -63,7 +63,9 @@ typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,        /* a required pointer is NULL                      */
   KDA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be,
-                               or too large                                    */
+                               or too large: t_total <= 2^31 - 65, and for a
+                               prefill n_seqs * n_heads * (dk / 16) and
+                               (t_total / chunk + n_seqs) * n_heads below 2^31 */
   KDA_ERR_DTYPE = -3,       /* dtype is not one of kda_dtype                   */
   KDA_ERR_UNSUPPORTED = -4, /* head dim, chunk size or plan not supported     */
   KDA_ERR_ALIGN = -5,       /* a pointer breaks its alignment rule (below)     */

@@ -84,6 +84,10 @@ def _valid_prefill(abi, **over):
     (dict(dtype=0), -3), (dict(dtype=3), -3), (dict(n_seqs=0), -2), (dict(n_heads=0), -2),
     (dict(t_total=-1), -2), (dict(dk=96, dv=96), -4), (dict(dk=128, dv=64), -4),
     (dict(chunk=48), -4), (dict(dtype=1, chunk=64), -4),
+    # grid and item counts past 32 bits: 20M sequences x 32 heads x 8 column
+    # blocks of the scan; 134M chunks of 16 tokens x 65535 heads
+    (dict(n_seqs=20_000_000, n_heads=32), -2),
+    (dict(t_total=(1 << 31) - 100, chunk=16, n_heads=65535), -2),
 ])
 def test_workspace_query_validation(abi, over, status):
     d = _valid_prefill(abi, **over)
