@@ -79,8 +79,8 @@ def log(msg: str):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from committed counter runs, or None when absent or
+def measured_counter(kernel: str, field: str):
+    """A per-launch figure from committed counter runs, or None when absent or
     taken on a different version of the kernel sources."""
     try:
         with open(COUNTERS_FILE) as f:
@@ -90,7 +90,12 @@ def measured_traffic(kernel: str):
     if data.get("source_hash") != kernel_source_hash():
         return None
     ent = data.get("kernels", {}).get(kernel)
-    return None if ent is None else ent.get("bytes_per_launch")
+    return None if ent is None else ent.get(field)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy)."""
+    return measured_counter(kernel, "bytes_per_launch")
 
 
 def to_dev(arr, torch):
@@ -257,6 +262,7 @@ def bench_recurrent(args, torch, kda, inp, state0, dec, stream, R=16):
     recurrent-prefill call on the carried state (a state pool, slot n for
     sequence n), against R decode steps doing the same work."""
     N, H, D = state0.shape[0], inp.H, inp.dk
+    R = min(R, next(iter(dec.values())).shape[0])  # no more tokens than the decode steps drew
     packed = {kk: t[:R].transpose(0, 1).reshape(N * R, *t.shape[2:]).contiguous()
               for kk, t in dec.items()}
     cu = torch.arange(0, N * R + 1, R, dtype=torch.int32, device="cuda")
@@ -485,6 +491,7 @@ def main():
     call_ms = stage_ms["prefill_call"]
     achieved = alg_bytes / (call_ms / 1e3) / 1e9
     traffic = measured_traffic("prefill")
+    mfma_cnt = measured_counter("prefill", "mfma_bf16_flop_per_launch")
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -492,6 +499,9 @@ def main():
         "scope": "whole prefill pass (chunk map + chunk-local + state scan), "
                  f"{alg_bytes} algorithmic bytes per pass",
         "mfma_frac": round(alg_flops / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        # bf16 MFMA flops the kernels issue per pass (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+        "mfma_frac_counters": (None if mfma_cnt is None else
+                               round(mfma_cnt / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
         "kernels_ms": {kname: round(v, 4) for kname, v in stage_ms.items()},
         "plan": args.plan,
         "dominant_kernel": max(["fused_or_chunk_local", "state_scan"], key=lambda kn: stage_ms[kn]),
