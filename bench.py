@@ -64,7 +64,8 @@ KERNEL_SOURCES = ["gated_delta_rule_55_amd/csrc/kda_prefill.hip",
                   "gated_delta_rule_55_amd/csrc/kda_conv.hip",
                   "gated_delta_rule_55_amd/csrc/kda_chunk_ops.h",
                   "gated_delta_rule_55_amd/csrc/kda_decode.hip",
-                  "gated_delta_rule_55_amd/csrc/kda_device.h"]
+                  "gated_delta_rule_55_amd/csrc/kda_device.h",
+                  "gated_delta_rule_55_amd/build.py"]  # its flags shape the kernels too
 
 
 def kernel_source_hash() -> str:

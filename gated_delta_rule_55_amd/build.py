@@ -24,6 +24,16 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source flags.  The prefill kernels are latency-bound; LLVM's iterative
+# ILP scheduler orders the chunk-local stage's phases better (measured on
+# MI355X at 32k tokens x 32 heads: chunk-local 0.661 -> 0.646 ms, the state
+# scan 0.583 -> 0.586 ms, the pass 1.251 -> 1.240 ms; results are unchanged, since
+# only the instruction order differs).
+SOURCE_FLAGS = {
+    "kda_prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def _hipcc():
     p = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     return p if os.path.exists(p) else "hipcc"
@@ -38,7 +48,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [_hipcc()] + HIPCC_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([_hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + lang +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
