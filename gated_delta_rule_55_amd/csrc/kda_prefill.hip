@@ -176,13 +176,19 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
   using Gm = Geo<TIO, D, C>;
   extern __shared__ __align__(16) unsigned char lds[];
   const int n_items = *chunk_total * n_heads;
+  // Items run from the last chunk to the first: the blocks written last are
+  // still in the Infinity Cache when the scan starts, and it reads the first
+  // chunks first.
+  auto item = [&](int w) { return n_items - 1 - w; };
   auto fetch = [&](typename CL::Inputs& in, int w) {
-    const ChunkEnt ent = tab[w / n_heads];
-    CL::prefetch(in, q, k, v, dec, beta, n_heads, w % n_heads, ent.start, ent.len, qk);
+    const int it = item(w);
+    const ChunkEnt ent = tab[it / n_heads];
+    CL::prefetch(in, q, k, v, dec, beta, n_heads, it % n_heads, ent.start, ent.len, qk);
   };
   auto compute = [&](const typename CL::Inputs& in, int w) {
-    const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)w * Gm::OUT_BYTES);
-    CL::run(lds, in, scale, out, q, k, dec, n_heads, w % n_heads, qk);
+    const int it = item(w);
+    const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)it * Gm::OUT_BYTES);
+    CL::run(lds, in, scale, out, q, k, dec, n_heads, it % n_heads, qk);
     __syncthreads();  // the next item overwrites the LDS
   };
   typename CL::Inputs cur, nxt;
