@@ -43,8 +43,8 @@ constexpr int kErrSync = -11;              // KDA_ERR_SYNC
 constexpr unsigned kSpinLimit = 1u << 24;  // polls before a wait gives up
 
 // Workspace: [header 256 B: status][chunk_off (N+1) int][chunk table NTU]
-// then the fused plan's flags and ring, or the two-pass plan's NTU * H output
-// blocks (the workspace is sized for the larger of the two).
+// then the fused plan's flags and ring (reserved only when that plan is
+// asked for), or the two-pass plan's NTU * H output blocks.
 struct WsLayout {
   size_t off_chunk_off, off_tab, off_flags, off_ring, off_blocks, total;
 };
@@ -61,7 +61,7 @@ struct Team {
 inline int nteams_cap(int d) { return 2048 / (d / 16); }
 
 template <typename TIO, int D, int C>
-WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu) {
+WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu, bool fused) {
   using Gm = Geo<TIO, D, C>;
   constexpr int R = Team<D>::R;
   WsLayout L;
@@ -74,7 +74,7 @@ WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu) {
   const size_t fused_end = L.off_ring + nteams * R * Gm::OUT_BYTES;
   L.off_blocks = after_tab;
   const size_t twopass_end = L.off_blocks + (size_t)ntu * n_heads * Gm::OUT_BYTES;
-  L.total = align_up(cmaxz(fused_end, twopass_end), 256);
+  L.total = align_up(fused ? cmaxz(fused_end, twopass_end) : twopass_end, 256);
   return L;
 }
 
@@ -629,7 +629,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
   } else {
     constexpr int R = Team<D>::R;
     const int64_t ntu = max_chunks(a.t_total, a.n_seqs, C);
-    const WsLayout L = ws_layout<TIO, D, C>(a.n_seqs, a.n_heads, ntu);
+    const WsLayout L = ws_layout<TIO, D, C>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     int* status = reinterpret_cast<int*>(ws + kWsStatusOffset);
     int* chunk_off = reinterpret_cast<int*>(ws + L.off_chunk_off);
@@ -724,9 +724,9 @@ template <typename TIO, int D>
 size_t ws_bytes_c(const PrefillArgs& a) {
   const int64_t ntu = max_chunks(a.t_total, a.n_seqs, a.chunk);
   switch (a.chunk) {
-    case 16: return ws_layout<TIO, D, 16>(a.n_seqs, a.n_heads, ntu).total;
-    case 32: return ws_layout<TIO, D, 32>(a.n_seqs, a.n_heads, ntu).total;
-    case 64: return ws_layout<TIO, D, 64>(a.n_seqs, a.n_heads, ntu).total;
+    case 16: return ws_layout<TIO, D, 16>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
+    case 32: return ws_layout<TIO, D, 32>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
+    case 64: return ws_layout<TIO, D, 64>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
   }
   return 0;
 }
