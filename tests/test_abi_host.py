@@ -96,6 +96,18 @@ def test_workspace_query_validation(abi, over, status):
     assert st.value == status and n == 0
 
 
+def test_workspace_two_pass_layout(abi):
+    """The two-pass workspace is the chunk table plus one block of chunk-local
+    results (80.5 KiB at d = 128, C = 64) per (chunk, head); nothing is
+    reserved for the switched-off fused plan."""
+    block = 82432
+    small = abi.workspace_bytes(_valid_prefill(abi, t_total=64, n_heads=1))
+    big = abi.workspace_bytes(_valid_prefill(abi, t_total=64 * 1001, n_heads=1))
+    # t_total / C + 1 chunk bound: 2 chunks -> 1002 chunks, one head
+    assert big - small >= 1000 * block and big - small < 1000 * block + 64 * 1024
+    assert small < 4 * block + 64 * 1024
+
+
 def test_workspace_query_sizes(abi):
     d = _valid_prefill(abi)
     n = abi.workspace_bytes(d)
