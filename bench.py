@@ -151,12 +151,12 @@ def bench_prefill(args, torch, kda, synth, inp=None, fused_gate=False):
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    # events: before the chunk map, after it, after the next launch, after the
-    # last launch (the fused plan has a single launch after the chunk map)
-    stage = {"chunk_map": [], "fused_or_chunk_local": [], "state_scan": [], "prefill_call": []}
+    # events: before the chunk map, after it, after the chunk-local stage,
+    # after the state scan
+    stage = {"chunk_map": [], "chunk_local": [], "state_scan": [], "prefill_call": []}
     for row in ev:
         stage["chunk_map"].append(row[0].elapsed_time(row[1]))
-        stage["fused_or_chunk_local"].append(row[1].elapsed_time(row[2]))
+        stage["chunk_local"].append(row[1].elapsed_time(row[2]))
         stage["state_scan"].append(row[2].elapsed_time(row[3]))
         stage["prefill_call"].append(row[0].elapsed_time(row[3]))
     avg = {kname: statistics.mean(vals) for kname, vals in stage.items()}
@@ -464,7 +464,7 @@ def main():
     ap.add_argument("--no-gate", action="store_true", help="skip the fused-gate prefill leg")
     ap.add_argument("--no-conv", action="store_true", help="skip the causal conv leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--plan", choices=["auto", "fused", "two_pass"], default="auto",
+    ap.add_argument("--plan", choices=["auto", "two_pass"], default="auto",
                     help="prefill launch plan")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -505,7 +505,7 @@ def main():
                                round(mfma_cnt / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
         "kernels_ms": {kname: round(v, 4) for kname, v in stage_ms.items()},
         "plan": args.plan,
-        "dominant_kernel": max(["fused_or_chunk_local", "state_scan"], key=lambda kn: stage_ms[kn]),
+        "dominant_kernel": max(["chunk_local", "state_scan"], key=lambda kn: stage_ms[kn]),
     }
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,

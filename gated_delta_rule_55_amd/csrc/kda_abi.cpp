@@ -121,9 +121,8 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
       d->plan != KDA_PLAN_AUTO && d->plan != KDA_PLAN_FUSED && d->plan != KDA_PLAN_TWO_PASS)
     return KDA_ERR_UNSUPPORTED;
   if (d->gate.mode != KDA_GATE_GIVEN && d->gate.mode != KDA_GATE_KIMI) return KDA_ERR_UNSUPPORTED;
-  // The fused plan is switched off: its workgroups wait on each other, and a
-  // run of it left a GPU unusable without an explained cause.  It stays
-  // rejected here, before anything is launched, until that is understood.
+  // The fused plan (value reserved) is not built: the chunked prefill runs as
+  // the three launches of the two-pass plan only.
   if (chunked && d->plan == KDA_PLAN_FUSED) return KDA_ERR_UNSUPPORTED;
   const int sq = check_qk(d->n_k_heads, d->qk_l2norm, d->n_heads, &a->qk);
   if (sq != KDA_OK) return sq;
@@ -303,7 +302,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_VERSION: return "descriptor struct_size mismatch";
     case KDA_ERR_ALIAS: return "output overlaps an input";
     case KDA_ERR_SEQLENS: return "cu_seqlens content invalid";
-    case KDA_ERR_SYNC: return "fused prefill workgroups timed out waiting on each other";
+    case KDA_ERR_SYNC: return "reserved (no current kernel reports it)";
     default: return "unknown status";
   }
 }

@@ -4,7 +4,6 @@
 //               solve, W/U and the chunk's output operators
 //   ScanStep    one step of the inter-chunk state recurrence with the output
 //               fused in, split over the workgroup's four waves by dk slice
-// Both are used by the standalone kernels and by the fused kernel.
 //
 // Per chunk of L <= C tokens (rows r, i), with G the inclusive cumulative sum
 // of g over the chunk in base 2 (G = log2(e) cumsum(g)), so every decay factor
@@ -104,15 +103,10 @@ struct Geo {
   static constexpr size_t OFF_NRM = OFF_FLAG + 16;  // [2][C]: 1/|k_r|, 1/|q_r|
   static constexpr size_t LOCAL_LDS = align_up(OFF_NRM + (size_t)2 * C * 4, 16);
 
-  // Scan-step LDS (aliases the chunk-local region; the two never overlap).
+  // Scan-step V^T rows (tokens padded to a 32-slice, plus a 16-byte pad).
   static constexpr int VT_LD = KCP + TP;
-  static constexpr size_t SCAN_RED = (size_t)KBD * TT * 64 * 16;  // one of v / o partials
-  static constexpr int OS_LD = 16 + TP;  // o staging rows: 16 value columns + pad
-  static constexpr size_t OFF_OS = align_up(2 * SCAN_RED + (size_t)16 * VT_LD * sizeof(TIO), 16);
-  static constexpr size_t SCAN_LDS = OFF_OS + (size_t)C * OS_LD * sizeof(TIO);
-  static constexpr size_t FUSED_LDS = cmaxz(LOCAL_LDS, SCAN_LDS);
 
-  static constexpr bool FITS = FUSED_LDS <= 160 * 1024;
+  static constexpr bool FITS = LOCAL_LDS <= 160 * 1024;
 };
 
 template <typename TIO, int D, int C>
@@ -807,13 +801,10 @@ struct ScanStep {
 
   // Loads of one chunk's operators, in three groups that a step consumes in
   // turn (W and Q', then U and Ol, then Kg and Gam), so a step can refill each
-  // group as soon as it is done with it.  ALL: every wave of the workgroup
-  // holds a dk slice (else waves past the slices load nothing).
-  template <bool ALL>
+  // group as soon as it is done with it.
   static __device__ __forceinline__ void load_wq(Ops& op, const ChunkOut<TIO>& in) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    if (!ALL && w >= KBD) return;
 #pragma unroll
     for (int i = 0; i < NOWN; ++i)
 #pragma unroll
@@ -823,11 +814,9 @@ struct ScanStep {
         op.q[i][s] = load_frag8<TIO>(in.q + f);
       }
   }
-  template <bool ALL>
   static __device__ __forceinline__ void load_uo(Ops& op, const ChunkOut<TIO>& in, int jb) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    if (!ALL && w >= KBD) return;
 #pragma unroll
     for (int c = 0; c < NJ; ++c)
 #pragma unroll
@@ -843,12 +832,10 @@ struct ScanStep {
         }
       }
   }
-  template <bool ALL>
   static __device__ __forceinline__ void load_kg(Ops& op, const ChunkOut<TIO>& in) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int lg = lane >> 4;
-    if (!ALL && w >= KBD) return;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -858,21 +845,18 @@ struct ScanStep {
     op.gam[0] = *reinterpret_cast<const f32x4*>(Gc);
     op.gam[1] = *reinterpret_cast<const f32x4*>(Gc + 16);
   }
-  template <bool ALL>
   static __device__ __forceinline__ void load(Ops& op, const ChunkOut<TIO>& in, int jb) {
-    load_wq<ALL>(op, in);
-    load_uo<ALL>(op, in, jb);
-    load_kg<ALL>(op, in);
+    load_wq(op, in);
+    load_uo(op, in, jb);
+    load_kg(op, in);
   }
 
   // Publish this wave's state slices as B fragments for the next step (every
   // wave of the workgroup calls it; a barrier must follow before they are read).
-  static __device__ __forceinline__ void publish(unsigned char* lds, const f32x4 (&S)[NJ][2],
-                                                 bool active) {
+  static __device__ __forceinline__ void publish(unsigned char* lds, const f32x4 (&S)[NJ][2]) {
     FragT* Sx = reinterpret_cast<FragT*>(lds);
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    if (!active) return;
 #pragma unroll
     for (int c = 0; c < NJ; ++c) Sx[(c * KBD + w) * 64 + lane] = frag_from_d<TIO>(S[c][0], S[c][1]);
   }
@@ -880,15 +864,15 @@ struct ScanStep {
   // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
   // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Expects the
   // state slices published (publish(), then a barrier) and leaves them
-  // published for the next step.  Two workgroup barriers.  ALL: every wave
-  // of the workgroup holds a dk slice (no idle waves), which keeps the step
-  // free of divergent branches so the compiler can count outstanding loads
-  // exactly.  NTH: threads of the workgroup.  With `nxt` set, each group of
+  // published for the next step.  Two workgroup barriers.  The workgroup has
+  // one wave per dk slice, so the step has no divergent branch and the
+  // compiler can count outstanding loads exactly.  NTH: threads of the
+  // workgroup.  With `nxt` set, each group of
   // `op` is reloaded from *nxt as soon as the step has consumed it (the loads
   // then overlap the rest of the step); nxt_ent supplies the new token range.
   // live = false (uniform) runs the step without effect: no o rows are
   // written and S keeps its value; the refills still happen.
-  template <bool ALL, int NTH>
+  template <int NTH>
   static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[NJ][2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
                                               int jb, const ChunkOut<TIO>* nxt = nullptr,
@@ -902,9 +886,8 @@ struct ScanStep {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
-    const bool active = ALL || w < KBD;
 
-    if (active) {
+    {
 #pragma unroll
       for (int c = 0; c < NJ; ++c) {
         FragT sb[KBD];
@@ -931,8 +914,8 @@ struct ScanStep {
       }
     }
     if (nxt) {
-      load_wq<ALL>(op, *nxt);
-      load_uo<ALL>(op, *nxt, jb);
+      load_wq(op, *nxt);
+      load_uo(op, *nxt, jb);
     }
     __syncthreads();
     {
@@ -953,7 +936,7 @@ struct ScanStep {
         buffer_store16(val, orsrc, off);
       }
     }
-    if (active) {
+    {
 #pragma unroll
       for (int c = 0; c < NJ; ++c)
 #pragma unroll
@@ -969,9 +952,9 @@ struct ScanStep {
           for (int j = 0; j < 4; ++j) S[c][m][j] = live ? sn[j] : S[c][m][j];
         }
     }
-    publish(lds, S, active);
+    publish(lds, S);
     if (nxt) {
-      load_kg<ALL>(op, *nxt);
+      load_kg(op, *nxt);
       op.start = nxt_ent->start;
       op.len = nxt_ent->len;
     }

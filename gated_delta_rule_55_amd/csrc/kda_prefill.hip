@@ -6,31 +6,10 @@
 // W/U with per-key-channel exp2 decay, the inter-chunk state recurrence
 // delta_h, and a GLA-style output (page "spike(kimi-linear): chunk_kda prefill
 // AOT port -- kernel set + pinned-config recipe", commit message and section
-// Delivered).  Here the same arithmetic (kda_chunk_ops.h) runs in one of two
-// launch plans:
-//
-//   fused (default)  chunk_map, then ONE cooperative kernel.  The 16-column
-//                    blocks of a (sequence, head) form a team of D/16
-//                    workgroups placed on one XCD.  Member j computes the
-//                    chunk-local stage of every chunk s = j (mod team size) a
-//                    few chunks ahead and hands it to the team through a ring
-//                    of slots that stays in L2 / Infinity Cache; every member
-//                    then runs the state scan for its columns over each chunk.
-//                    The intermediates never make a round trip to HBM.
-//   two-pass         chunk_map, chunk_local over every (chunk, head) into a
-//                    full-size workspace, then state_scan.  Used when the
-//                    fused grid cannot be co-resident, or on request.
-//
-// The fused kernel's hand-off is a producer/consumer protocol per team:
-// ready[slot] = s + 1 once chunk s is written (agent-scope release), and
-// done[slot] counts the members that finished reading it.  Member j produces
-// the chunks s = j (mod N): those below LA before any consumption, then in
-// round r the one in [rN + LA, (r + 1)N + LA), into slot s mod R once the
-// slot's previous chunk has been read by all N members; then it consumes
-// chunks rN .. rN + N - 1.  With LA = N + 2 and R = 2N + 4 every wait refers
-// to work of a strictly earlier round of some member, so with all members
-// resident (cooperative launch) the team cannot deadlock.  Waits are bounded: on a
-// timeout the kernel records an error in the status word and exits.
+// Delivered).  Here the same arithmetic (kda_chunk_ops.h) runs in three
+// launches: the chunk map (varlen chunk table from the device cu_seqlens), the
+// chunk-local stage over every (chunk, head) into a workspace, and the state
+// scan with the output fused in, which reads the workspace back.
 #include "kda_chunk_ops.h"
 #include "kda_launch.h"
 
@@ -38,43 +17,23 @@ namespace kda {
 
 namespace {
 
-constexpr int kErrSeqlens = -10;           // KDA_ERR_SEQLENS
-constexpr int kErrSync = -11;              // KDA_ERR_SYNC
-constexpr unsigned kSpinLimit = 1u << 24;  // polls before a wait gives up
+constexpr int kErrSeqlens = -10;  // KDA_ERR_SEQLENS
 
 // Workspace: [header 256 B: status][chunk_off (N+1) int][chunk table NTU]
-// then the fused plan's flags and ring (reserved only when that plan is
-// asked for), or the two-pass plan's NTU * H output blocks.
+// [blocks: H x NTU chunk-local result blocks, head-major, so the chunks of
+// one head that the scan walks in order are contiguous].
 struct WsLayout {
-  size_t off_chunk_off, off_tab, off_flags, off_ring, off_blocks, total;
+  size_t off_chunk_off, off_tab, off_blocks, total;
 };
-
-// Team geometry of the fused kernel.
-template <int D>
-struct Team {
-  static constexpr int N = D / 16;     // members (16-column blocks)
-  static constexpr int LA = N + 2;     // produce this many chunks ahead
-  static constexpr int R = 2 * N + 4;  // ring slots
-};
-
-// Largest team count any launch may use (bounds the workspace).
-inline int nteams_cap(int d) { return 2048 / (d / 16); }
 
 template <typename TIO, int D, int C>
-WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu, bool fused) {
+WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu) {
   using Gm = Geo<TIO, D, C>;
-  constexpr int R = Team<D>::R;
   WsLayout L;
   L.off_chunk_off = 256;
   L.off_tab = align_up(L.off_chunk_off + sizeof(int) * (size_t)(n_seqs + 1), 256);
-  const size_t after_tab = align_up(L.off_tab + sizeof(ChunkEnt) * (size_t)ntu, 256);
-  const size_t nteams = (size_t)nteams_cap(D);
-  L.off_flags = after_tab;
-  L.off_ring = align_up(L.off_flags + sizeof(int) * 2 * nteams * R, 256);
-  const size_t fused_end = L.off_ring + nteams * R * Gm::OUT_BYTES;
-  L.off_blocks = after_tab;
-  const size_t twopass_end = L.off_blocks + (size_t)ntu * n_heads * Gm::OUT_BYTES;
-  L.total = align_up(fused ? cmaxz(fused_end, twopass_end) : twopass_end, 256);
+  L.off_blocks = align_up(L.off_tab + sizeof(ChunkEnt) * (size_t)ntu, 256);
+  L.total = align_up(L.off_blocks + (size_t)ntu * n_heads * Gm::OUT_BYTES, 256);
   return L;
 }
 
@@ -83,18 +42,16 @@ WsLayout ws_layout(int n_seqs, int n_heads, int64_t ntu, bool fused) {
 // non-decreasing, cu[N] = T, chunk count within the bound) and writes, for
 // every chunk, its sequence, first token, length and index within the
 // sequence.  On invalid offsets no chunk is emitted and the status word says
-// so.  Also clears the fused kernel's ring flags.
+// so.
 __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restrict__ cu,
                                                         int n_seqs, int64_t t_total, int chunk,
                                                         int64_t ntu, int* __restrict__ status,
                                                         int* __restrict__ chunk_off,
-                                                        ChunkEnt* __restrict__ tab,
-                                                        int* __restrict__ flags, int n_flags) {
+                                                        ChunkEnt* __restrict__ tab) {
   __shared__ int s_bad;
   __shared__ int s_scan[256];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
-  for (int i = tid; i < n_flags; i += 256) flags[i] = 0;
   if (tid == 0) {
     s_bad = 0;
     s_carry = 0;
@@ -171,7 +128,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     DecayIn<TIO> dec, const TIO* __restrict__ beta, int n_heads, QkIn qk, float scale,
     const int* __restrict__ chunk_total, const ChunkEnt* __restrict__ tab,
-    unsigned char* __restrict__ blocks) {
+    unsigned char* __restrict__ blocks, int ntu) {
   using CL = ChunkLocal<TIO, D, C, GATE>;
   using Gm = Geo<TIO, D, C>;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -187,7 +144,8 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
   };
   auto compute = [&](const typename CL::Inputs& in, int w) {
     const int it = item(w);
-    const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(blocks + (size_t)it * Gm::OUT_BYTES);
+    const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(
+        blocks + ((size_t)(it % n_heads) * ntu + it / n_heads) * Gm::OUT_BYTES);
     CL::run(lds, in, scale, out, q, k, dec, n_heads, it % n_heads, qk);
     __syncthreads();  // the next item overwrites the LDS
   };
@@ -237,7 +195,7 @@ template <typename TIO, int D, int C, int NJ>
 __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     const void* __restrict__ h0, void* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
     int n_heads, const int* __restrict__ status, const int* __restrict__ chunk_off,
-    const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks,
+    const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks, int ntu,
     const int* __restrict__ slots, int n_slots, int state_bf16) {
   using Gm = Geo<TIO, D, C>;
   using SS = ScanStep<TIO, D, C, NJ>;
@@ -293,12 +251,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(S[c][m][j]));
-  SS::publish(lds, S, true);  // read by the first step after the barrier below
+  SS::publish(lds, S);  // read by the first step after the barrier below
 
   const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
   const int64_t ostride = (int64_t)n_heads * D;
   auto out_of = [&](int ci) {
-    return chunk_out_at<TIO, D, C>(blocks + ((size_t)ci * n_heads + h) * Gm::OUT_BYTES);
+    return chunk_out_at<TIO, D, C>(blocks + ((size_t)h * ntu + ci) * Gm::OUT_BYTES);
   };
   // Three chunks of operators in flight: each buffer keeps its role across the
   // unrolled loop, so no load waits on a later one.
@@ -312,7 +270,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   auto clamp = [&](int ci) { return ci < c_end ? ci : c_end - 1; };
   auto fetch = [&](typename SS::Ops& buf, int ci) {
     ci = clamp(ci);
-    SS::template load<true>(buf, out_of(ci), jb);
+    SS::load(buf, out_of(ci), jb);
     buf.start = tab[ci].start;
     buf.len = tab[ci].len;
   };
@@ -335,7 +293,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   auto run_step = [&](typename SS::Ops& buf, int ci) {
     const int cn = clamp(ci + 3);
     const ChunkOut<TIO> nx = out_of(cn);
-    SS::template step<true, NTH>(lds, S, buf, o, ostride, h, jb, &nx, tab + cn, ci < c_end);
+    SS::template step<NTH>(lds, S, buf, o, ostride, h, jb, &nx, tab + cn, ci < c_end);
   };
   for (int ci = c_begin; ci < c_end; ci += 3) {
     run_step(b0, ci);
@@ -357,233 +315,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Fused plan.
-struct FusedArgs {
-  const void *q, *k, *v;
-  const float* g;
-  const void* beta;
-  const float* h0;
-  float* ht;
-  void* o;
-  int n_seqs, n_heads, nteams;
-  QkIn qk;
-  float scale;
-  int* status;
-  const int* chunk_off;
-  const ChunkEnt* tab;
-  int* flags;  // [nteams][R] ready, then [nteams][R] done
-  unsigned char* ring;
-};
-
-// Position in a team's sequence of chunks: tasks t = team + i * nteams (task
-// = n * H + h), their chunks in order.
-struct Cursor {
-  int i;       // task ordinal within the team
-  int n, h;    // the task
-  int cb, ce;  // its global chunk range
-  int ci;      // current global chunk
-  bool end;
-};
-
-__device__ __forceinline__ void cursor_task(Cursor& c, int i, int team, const FusedArgs& a) {
-  const int task = team + i * a.nteams;
-  c.i = i;
-  c.end = task >= a.n_seqs * a.n_heads;
-  if (c.end) return;
-  c.n = task / a.n_heads;
-  c.h = task % a.n_heads;
-  c.cb = a.chunk_off[c.n];
-  c.ce = a.chunk_off[c.n + 1];
-  c.ci = c.cb;
-}
-
-// Skip to the next task that still has chunks.
-__device__ __forceinline__ void cursor_settle(Cursor& c, int team, const FusedArgs& a) {
-  while (!c.end && c.ci >= c.ce) cursor_task(c, c.i + 1, team, a);
-}
-
-__device__ __forceinline__ int spin_until_geq(const int* p, int target, int* status) {
-  unsigned n = 0;
-  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    if (++n > kSpinLimit) {
-      __hip_atomic_store(status, kErrSync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return 0;
-    }
-    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return 0;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return 1;
-}
-
-template <typename TIO, int D, int C>
-__global__ __launch_bounds__(kLocalThreads) void fused_kernel(FusedArgs a) {
-  using Gm = Geo<TIO, D, C>;
-  using CL = ChunkLocal<TIO, D, C>;
-  using SS = ScanStep<TIO, D, C>;
-  constexpr int NB = Team<D>::N, LA = Team<D>::LA, R = Team<D>::R;
-  extern __shared__ __align__(16) unsigned char lds[];
-  __shared__ int s_ok;
-
-  if (a.status[0] != 0) return;
-  const TIO* q = static_cast<const TIO*>(a.q);
-  const TIO* k = static_cast<const TIO*>(a.k);
-  const TIO* v = static_cast<const TIO*>(a.v);
-  const TIO* beta = static_cast<const TIO*>(a.beta);
-  TIO* o = static_cast<TIO*>(a.o);
-  const DecayIn<TIO> dec{a.g, nullptr, nullptr, nullptr};
-
-  // team / member, XCD-aware: members of a team share blockIdx mod 8
-  const int G = gridDim.x;
-  int y = blockIdx.x;
-  if (G % (8 * NB) == 0) y = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
-  const int team = y / NB;
-  const int jb = y % NB;  // member = 16-column block of the scan
-  int* ready = a.flags + (size_t)team * R;
-  int* done = a.flags + (size_t)a.nteams * R + (size_t)team * R;
-  unsigned char* ring = a.ring + (size_t)team * R * Gm::OUT_BYTES;
-  auto slot_out = [&](int s) {
-    return chunk_out_at<TIO, D, C>(ring + (size_t)(s % R) * Gm::OUT_BYTES);
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
-  const int64_t ostride = (int64_t)a.n_heads * D;
-
-  // total chunks of the team
-  int total = 0;
-  for (int i = 0;; ++i) {
-    const int task = team + i * a.nteams;
-    if (task >= a.n_seqs * a.n_heads) break;
-    const int n = task / a.n_heads;
-    total += a.chunk_off[n + 1] - a.chunk_off[n];
-  }
-
-  // ---- producer: chunks s = jb (mod NB), LA ahead of consumption -----------
-  Cursor pc;
-  cursor_task(pc, 0, team, a);
-  cursor_settle(pc, team, a);
-  int ps = 0;  // team sequence number of pc
-  auto advance = [&](int by) {
-    for (int t = 0; t < by && !pc.end; ++t) {
-      ++pc.ci;
-      ++ps;
-      cursor_settle(pc, team, a);
-    }
-  };
-  advance(jb);
-  typename CL::Inputs in;
-  bool have_in = false;
-  auto prefetch_next = [&]() {
-    have_in = !pc.end;
-    if (have_in) {
-      const ChunkEnt ent = a.tab[pc.ci];
-      CL::prefetch(in, q, k, v, dec, beta, a.n_heads, pc.h, ent.start, ent.len, a.qk);
-    }
-  };
-  // Produce chunk ps from `in`, publish it, step to this member's next chunk
-  // and start loading its inputs.
-  auto produce = [&](bool wait_slot) -> bool {
-    if (wait_slot) {
-      if (tid == 0) s_ok = spin_until_geq(done + ps % R, NB * (ps / R), a.status);
-      __syncthreads();
-      if (!s_ok) return false;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    CL::run(lds, in, a.scale, slot_out(ps), q, k, dec, a.n_heads, pc.h, a.qk);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // every wave's stores
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(ready + ps % R, ps + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    advance(NB);
-    prefetch_next();
-    return true;
-  };
-  prefetch_next();
-  while (have_in && ps < LA)  // prologue: fresh slots
-    if (!produce(false)) return;
-
-  // ---- consumer: every chunk, this member's 16 columns ----------------------
-  Cursor cc;
-  cursor_task(cc, 0, team, a);
-  f32x4 S[1][2];
-  auto state_in = [&]() {
-    const size_t sb = ((size_t)cc.n * a.n_heads + cc.h) * D * D;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        S[0][m][j] = (a.h0 && w < Gm::KBD)
-                      ? a.h0[sb + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16]
-                      : 0.f;
-  };
-  auto state_out = [&]() {
-    if (!a.ht || w >= Gm::KBD) return;
-    const size_t sb = ((size_t)cc.n * a.n_heads + cc.h) * D * D;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a.ht[sb + (size_t)(32 * w + 16 * m + 4 * lg + j) * D + 16 * jb + l16] = S[0][m][j];
-  };
-  // Enter the task under cc; empty tasks pass h0 through to ht.
-  auto enter_tasks = [&]() {
-    while (!cc.end) {
-      state_in();
-      if (cc.cb < cc.ce) return;
-      state_out();
-      cursor_task(cc, cc.i + 1, team, a);
-    }
-  };
-  enter_tasks();
-
-  typename SS::Ops cur, nxt;
-  for (int r = 0; r * NB < total; ++r) {
-    // produce this member's chunk of the round: the one in
-    // [rN + LA, (r + 1)N + LA), i.e. rN + LA + ((jb - LA) mod N)
-    if (have_in && ps < (r + 1) * NB + LA)
-      if (!produce(true)) return;
-    // wait until this round's chunks and the next one are ready
-    const int s0 = r * NB, s1 = min(s0 + NB, total), sw = min(s1 + 1, total);
-    if (tid == 0) {
-      int ok = 1;
-      for (int s = s0; s < sw && ok; ++s) ok = spin_until_geq(ready + s % R, s + 1, a.status);
-      s_ok = ok;
-    }
-    __syncthreads();
-    if (!s_ok) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    SS::clear_vt(lds);  // the chunk-local stage used this LDS
-    SS::publish(lds, S, w < Gm::KBD);
-    if (s0 == 0) SS::template load<false>(cur, slot_out(0), jb);
-    __syncthreads();
-    for (int s = s0; s < s1; ++s) {
-      if (s + 1 < sw) SS::template load<false>(nxt, slot_out(s + 1), jb);
-      cur.start = a.tab[cc.ci].start;
-      cur.len = a.tab[cc.ci].len;
-      SS::template step<false, kLocalThreads>(lds, S, cur, o, ostride, cc.h, jb);
-      cur = nxt;
-      ++cc.ci;
-      if (cc.ci >= cc.ce) {  // task finished (uniform over the workgroup)
-        state_out();
-        cursor_task(cc, cc.i + 1, team, a);
-        enter_tasks();
-        SS::publish(lds, S, w < Gm::KBD);  // the next task's start state
-        __syncthreads();
-      }
-    }
-    // release the round's slots: every wave's reads are complete
-    __syncthreads();
-    if (tid < s1 - s0)
-      __hip_atomic_fetch_add(done + (s0 + tid) % R, 1, __ATOMIC_RELEASE,
-                             __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 template <typename TIO, int D, int C, int NJ>
 hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk_off,
-                       const ChunkEnt* tab, unsigned char* blocks, hipStream_t stream) {
+                       const ChunkEnt* tab, unsigned char* blocks, int ntu, hipStream_t stream) {
   using SS = ScanStep<TIO, D, C, NJ>;
   static_assert(SS::LDS_BYTES <= 160 * 1024, "scan LDS");
   hipError_t err = hipFuncSetAttribute((const void*)state_scan_kernel<TIO, D, C, NJ>,
@@ -593,31 +327,8 @@ hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk
   const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * SS::NB);
   hipLaunchKernelGGL((state_scan_kernel<TIO, D, C, NJ>), dim3(nblk), dim3(64 * (D / 32)),
                      SS::LDS_BYTES, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
-                     chunk_off, tab, blocks, a.slots, a.n_slots, (int)a.state_bf16);
+                     chunk_off, tab, blocks, ntu, a.slots, a.n_slots, (int)a.state_bf16);
   return hipGetLastError();
-}
-
-template <typename TIO, int D, int C>
-int fused_teams(int n_seqs, int n_heads) {
-  using Gm = Geo<TIO, D, C>;
-  constexpr int NB = D / 16;
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipFuncSetAttribute((const void*)fused_kernel<TIO, D, C>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)Gm::FUSED_LDS) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<TIO, D, C>,
-                                                   kLocalThreads, Gm::FUSED_LDS) != hipSuccess)
-    return 0;
-  const int tasks = n_seqs * n_heads;
-  int nteams = cus * per_cu / NB;
-  if (nteams > nteams_cap(D)) nteams = nteams_cap(D);
-  if (nteams > tasks) nteams = tasks;
-  if (nteams >= 8) nteams -= nteams % 8;  // whole teams per XCD
-  return nteams;
 }
 
 template <typename TIO, int D, int C>
@@ -627,59 +338,19 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
   if constexpr (!Gm::FITS) {
     return hipErrorInvalidValue;
   } else {
-    constexpr int R = Team<D>::R;
     const int64_t ntu = max_chunks(a.t_total, a.n_seqs, C);
-    const WsLayout L = ws_layout<TIO, D, C>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_);
+    const WsLayout L = ws_layout<TIO, D, C>(a.n_seqs, a.n_heads, ntu);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     int* status = reinterpret_cast<int*>(ws + kWsStatusOffset);
     int* chunk_off = reinterpret_cast<int*>(ws + L.off_chunk_off);
     ChunkEnt* tab = reinterpret_cast<ChunkEnt*>(ws + L.off_tab);
-    int* flags = reinterpret_cast<int*>(ws + L.off_flags);
-
-    // AUTO takes the two-pass plan: on the measured workloads it is faster than
-    // the fused kernel as the chunk-local stage stands today.
-    int nteams = 0;
-    if (a.plan == KDA_PLAN_FUSED_) nteams = fused_teams<TIO, D, C>(a.n_seqs, a.n_heads);
-    const bool fused = nteams > 0;
-    if (!fused && a.plan == KDA_PLAN_FUSED_) return hipErrorCooperativeLaunchTooLarge;
 
     hipError_t err = hipSuccess;
     if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(256), 0, stream, a.cu_seqlens, a.n_seqs,
-                       a.t_total, C, ntu, status, chunk_off, tab, flags,
-                       fused ? 2 * nteams * R : 0);
+                       a.t_total, C, ntu, status, chunk_off, tab);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
-
-    if (fused) {
-      FusedArgs fa;
-      fa.q = a.q;
-      fa.k = a.k;
-      fa.v = a.v;
-      fa.g = a.g;
-      fa.beta = a.beta;
-      fa.h0 = static_cast<const float*>(a.h0);  // fp32 states only on this plan
-      fa.ht = static_cast<float*>(a.ht);
-      fa.o = a.o;
-      fa.n_seqs = a.n_seqs;
-      fa.n_heads = a.n_heads;
-      fa.qk = QkIn{a.qk.kheads, a.qk.norm};
-      fa.nteams = nteams;
-      fa.scale = a.scale;
-      fa.status = status;
-      fa.chunk_off = chunk_off;
-      fa.tab = tab;
-      fa.flags = flags;
-      fa.ring = ws + L.off_ring;
-      void* args[] = {&fa};
-      err = hipLaunchCooperativeKernel((const void*)fused_kernel<TIO, D, C>,
-                                       dim3((unsigned)(nteams * (D / 16))), dim3(kLocalThreads),
-                                       args, (unsigned)Gm::FUSED_LDS, stream);
-      if (err != hipSuccess) return err;
-      if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
-      if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
-      return hipSuccess;
-    }
 
     unsigned char* blocks = ws + L.off_blocks;
     const bool gate = a.gate.mode == GATE_KIMI_;
@@ -701,18 +372,20 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
       hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, true>), dim3(grid), dim3(kLocalThreads),
                          Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
                          (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
-                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks);
+                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks,
+                         (int)ntu);
     else
       hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, false>), dim3(grid), dim3(kLocalThreads),
                          Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
                          (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
-                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks);
+                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks,
+                         (int)ntu);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
     switch (scan_tiles<TIO, D>(a.n_seqs, a.n_heads, cus)) {
-      case 4: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 4>>(a, status, chunk_off, tab, blocks, stream); break;
-      case 2: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 2>>(a, status, chunk_off, tab, blocks, stream); break;
-      default: err = launch_scan<TIO, D, C, 1>(a, status, chunk_off, tab, blocks, stream); break;
+      case 4: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 4>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+      case 2: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 2>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+      default: err = launch_scan<TIO, D, C, 1>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
     }
     if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;
@@ -724,9 +397,9 @@ template <typename TIO, int D>
 size_t ws_bytes_c(const PrefillArgs& a) {
   const int64_t ntu = max_chunks(a.t_total, a.n_seqs, a.chunk);
   switch (a.chunk) {
-    case 16: return ws_layout<TIO, D, 16>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
-    case 32: return ws_layout<TIO, D, 32>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
-    case 64: return ws_layout<TIO, D, 64>(a.n_seqs, a.n_heads, ntu, a.plan == KDA_PLAN_FUSED_).total;
+    case 16: return ws_layout<TIO, D, 16>(a.n_seqs, a.n_heads, ntu).total;
+    case 32: return ws_layout<TIO, D, 32>(a.n_seqs, a.n_heads, ntu).total;
+    case 64: return ws_layout<TIO, D, 64>(a.n_seqs, a.n_heads, ntu).total;
   }
   return 0;
 }

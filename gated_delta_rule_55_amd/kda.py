@@ -158,9 +158,9 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     None (one sequence).  Returns (o [T, H, dv], ht [N, H, dk, dv] or None).
     `ht` may be h0 itself (in-place carry).  `events`: four torch.cuda.Event
     objects recorded before the first launch and after each of the three
-    launches (chunk map, chunk-local stage, state scan), for stage timing (the
-    fused plan has one launch after the chunk map; its time is reported as the
-    chunk-local stage).  `plan`: "auto", "fused" or "two_pass".  `gate`: None
+    launches (chunk map, chunk-local stage, state scan), for stage timing.
+    `plan`: "auto" or "two_pass" (the same plan; "fused" is a reserved value
+    the library refuses).  `gate`: None
     (g given), or (x [T, H, dk] in q's dtype, a_log [H] fp32, dt_bias [H, dk]
     fp32) to compute g = -exp(a_log) softplus(x + dt_bias) in the kernels
     (g may then be None).  `state_indices` (int32 [N] on the device): h0 and

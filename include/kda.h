@@ -75,9 +75,7 @@ typedef enum {
   KDA_ERR_ALIAS = -9,       /* an output overlaps an input it may not overlap  */
   KDA_ERR_SEQLENS = -10,    /* cu_seqlens content invalid (reported through
                                kda_workspace_status, never by a call's return) */
-  KDA_ERR_SYNC = -11        /* the fused plan's workgroups stopped waiting on
-                               each other (reported through kda_workspace_status);
-                               o and ht are incomplete */
+  KDA_ERR_SYNC = -11        /* reserved: no kernel of this version reports it */
 } kda_status;
 
 typedef enum { KDA_DTYPE_F32 = 1, KDA_DTYPE_BF16 = 2 } kda_dtype;
@@ -100,11 +98,11 @@ typedef struct {
   const float* dt_bias;       /* KIMI: [H, dk] fp32                             */
 } kda_gate_desc;
 
-/* Launch plan of the chunked prefill.  TWO_PASS writes the chunk-local
- * results to the workspace and reads them back in the state scan; AUTO
- * selects it.  FUSED (one cooperative kernel whose chunk-local results stay
- * in a cache-resident ring) is currently switched off: a request for it
- * returns KDA_ERR_UNSUPPORTED before anything is launched. */
+/* Launch plan of the chunked prefill.  TWO_PASS (what AUTO selects) writes
+ * the chunk-local results to the workspace and reads them back in the state
+ * scan.  FUSED is a reserved value: this library does not build such a plan,
+ * and a request for it returns KDA_ERR_UNSUPPORTED before anything is
+ * launched. */
 typedef enum { KDA_PLAN_AUTO = 0, KDA_PLAN_FUSED = 1, KDA_PLAN_TWO_PASS = 2 } kda_plan;
 
 /* Chunked prefill over a packed batch of N sequences (T_total tokens).

@@ -98,8 +98,7 @@ def test_workspace_query_validation(abi, over, status):
 
 def test_workspace_two_pass_layout(abi):
     """The two-pass workspace is the chunk table plus one block of chunk-local
-    results (80.5 KiB at d = 128, C = 64) per (chunk, head); nothing is
-    reserved for the switched-off fused plan."""
+    results (80.5 KiB at d = 128, C = 64) per (chunk, head)."""
     block = 82432
     small = abi.workspace_bytes(_valid_prefill(abi, t_total=64, n_heads=1))
     big = abi.workspace_bytes(_valid_prefill(abi, t_total=64 * 1001, n_heads=1))
@@ -192,8 +191,8 @@ def test_state_pool_and_recurrent_validation(abi):
 
 
 @no_gpu_only
-def test_fused_plan_is_switched_off(abi):
-    """A fused-plan request is refused on the host, before any launch."""
+def test_fused_plan_value_is_refused(abi):
+    """The reserved fused-plan value is refused on the host, before any launch."""
     d = _valid_prefill(abi, plan=abi.KDA_PLAN_FUSED)
     st = ctypes.c_int(0)
     abi.lib().kda_chunk_prefill_workspace_bytes(ctypes.byref(d), ctypes.byref(st))

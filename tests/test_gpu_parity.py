@@ -20,22 +20,15 @@ def kda():
     return m
 
 
-def run_prefill(kda, inp, chunk=None, ht_inplace=False, plan="auto"):
+def run_prefill(kda, inp, chunk=None, ht_inplace=False):
     d = dev_inputs(inp)
     ht = None
     if ht_inplace and d["h0"] is not None:
         ht = d["h0"]
     o, hT = kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
-                              d["cu_seqlens"], scale=inp.scale, chunk=chunk or inp.chunk, ht=ht,
-                              plan=plan)
+                              d["cu_seqlens"], scale=inp.scale, chunk=chunk or inp.chunk, ht=ht)
     torch.cuda.synchronize()
     return to_host64(o), to_host64(hT)
-
-
-# The fused plan is switched off in the library (a request for it returns
-# KDA_ERR_UNSUPPORTED): a run of it left a GPU unusable without an explained
-# cause, so its cases stay skipped until that is understood.
-FUSED_OFF = "fused plan switched off pending review of its inter-workgroup waits"
 
 
 @pytest.mark.parametrize("dtype,d,chunk,lengths,h0", [
@@ -49,32 +42,16 @@ FUSED_OFF = "fused plan switched off pending review of its inter-workgroup waits
     ("bf16", 128, 16, [90, 17], True),
     ("bf16", 128, 32, [150], False),
 ])
-@pytest.mark.parametrize("plan", [pytest.param("fused", marks=pytest.mark.skip(reason=FUSED_OFF)),
-                                  "two_pass"])
-def test_prefill_small(kda, dtype, d, chunk, lengths, h0, plan):
-    say(f"prefill plan={plan} dtype={dtype} d={d} C={chunk} lengths={lengths} h0={h0}")
+def test_prefill_small(kda, dtype, d, chunk, lengths, h0):
+    say(f"prefill dtype={dtype} d={d} C={chunk} lengths={lengths} h0={h0}")
     inp = synth.make_inputs(11, lengths, 3, d, dtype=dtype,
                             gate="softplus" if dtype == "f32" else "kimi",
                             h0_std=0.05 if h0 else 0.0, chunk=chunk)
-    o, hT = run_prefill(kda, inp, plan=plan)
+    o, hT = run_prefill(kda, inp)
     o_ref, hT_ref = oracle_prefill(inp)
     eo, es = rel_l2(o, o_ref), rel_l2(hT, hT_ref)
     say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
-
-
-@pytest.mark.skip(reason=FUSED_OFF)
-@pytest.mark.parametrize("lengths", [[300], [64, 1, 129, 0, 200, 640], [0, 0]])
-def test_plans_agree_bitwise(kda, lengths):
-    """The fused and two-pass plans run the same arithmetic in the same order,
-    so their outputs are identical bit for bit."""
-    say(f"fused vs two-pass, lengths={lengths}")
-    inp = synth.make_inputs(12, lengths, 5, 128, dtype="bf16", h0_std=0.05, chunk=64)
-    o1, s1 = run_prefill(kda, inp, plan="fused")
-    o2, s2 = run_prefill(kda, inp, plan="two_pass")
-    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
-    if sum(lengths) == 0:
-        assert np.array_equal(s1, inp.h0.astype(np.float64))
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 32), ("f32", 128), ("bf16", 64), ("bf16", 128)])
