@@ -25,9 +25,11 @@
 // and a Gram tile (a, b) is Lk_a . Rn_b^T times the per-channel factor
 // 2^(rho_a - rho_{b+1}): 1 for adjacent blocks, <= 1 for farther ones, and the
 // block's own decay span (>= 1) on the diagonal.  The diagonal factor is the
-// only one above 1; when it exceeds 2^64 for some channel the tile is summed
-// entry by entry from the inputs instead.  W, Kg and Q * 2^G reuse Lk, Rn and
-// Lq with one more per-channel factor, so each element costs two exp2.
+// only one above 1; when it exceeds 2^64 for some channel the block's tile is
+// summed entry by entry, each term with its own exact factor 2^(G[r]-G[i]) <= 1,
+// from the staged k, q and G before the scaled operands replace them.  W, Kg
+// and Q * 2^G reuse Lk, Rn and Lq with one more per-channel factor, so each
+// element costs two exp2.
 #pragma once
 
 #include "kda_device.h"
@@ -100,8 +102,14 @@ struct Geo {
   static constexpr size_t OFF_FAC = OFF_RHO + (size_t)(TT + 1) * D * 4;
   static constexpr size_t OFF_BETA = OFF_FAC + (size_t)NFAC * D * 4;
   static constexpr size_t OFF_FLAG = OFF_BETA + (size_t)C * 4;
-  static constexpr size_t OFF_NRM = OFF_FLAG + 16;  // [2][C]: 1/|k_r|, 1/|q_r|
-  static constexpr size_t LOCAL_LDS = align_up(OFF_NRM + (size_t)2 * C * 4, 16);
+  // Exact diagonal Gram tiles [TT][2][16][16] fp32 (A_kk, A_qk) for blocks
+  // whose decay span is too large to factor: in the T region (not in use
+  // until the triangular solve) when they fit there, else after the flags.
+  static constexpr size_t EXACT_BYTES = (size_t)TT * 2 * 256 * 4;
+  static constexpr bool EXACT_IN_T = EXACT_BYTES <= (size_t)C * TK_LD * sizeof(TIO);
+  static constexpr size_t OFF_EXACT = EXACT_IN_T ? OFF_TB : OFF_FLAG + 16;
+  static constexpr size_t LOCAL_LDS =
+      align_up(EXACT_IN_T ? OFF_FLAG + 16 : OFF_EXACT + EXACT_BYTES, 16);
 
   // Scan-step V^T rows (tokens padded to a 32-slice, plus a 16-byte pad).
   static constexpr int VT_LD = KCP + TP;
@@ -288,49 +296,6 @@ struct ChunkLocal {
     in.beta = beta[(tok0 + min(tid, L - 1)) * n_heads + h];
   }
 
-  // Entry-by-entry Gram tile from the inputs in global memory, for a diagonal
-  // tile whose decay span is too large to factor.  Lane holds rows
-  // 16a + 4lg + j, column 16a + l16 (accumulator layout).
-  // With q/k normalisation, nrm holds the row factors (1/|k_r| then 1/|q_r|).
-  static __device__ void exact_diag_tile(int a, f32x4& akk, f32x4& aqk,
-                                         const TIO* __restrict__ q, const TIO* __restrict__ k,
-                                         const DecayIn<TIO>& dec, float ea, int n_heads, int h,
-                                         int64_t tok0, int L, QkIn qk, const float* nrm) {
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15, lg = lane >> 4;
-    const int64_t rs = (int64_t)n_heads * D;
-    const int64_t ks = (int64_t)qk.kheads * D;
-    const int64_t kh = (int64_t)(h / (n_heads / qk.kheads)) * D;
-    const int ii = 16 * a + l16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rr = 16 * a + 4 * lg + j;
-      float sk = 0.f, sq = 0.f;
-      if (ii <= rr && rr < L) {
-        for (int c = 0; c < D; ++c) {
-          float e = 0.f;  // G[rr] - G[ii] = log2(e) x (sum of g over (ii, rr])
-          for (int t = ii + 1; t <= rr; ++t) {
-            const int64_t at = (tok0 + t) * rs + (int64_t)h * D + c;
-            if constexpr (GATE)
-              e += kimi_gate_log2(to_f32(dec.x[at]) + dec.dt_bias[(int64_t)h * D + c], ea);
-            else
-              e += dec.g[at] * kLog2e;
-          }
-          const float f = fast_exp2(e);
-          const float ki = to_f32(k[(tok0 + ii) * ks + kh + c]) * f;
-          sk += to_f32(k[(tok0 + rr) * ks + kh + c]) * ki;
-          sq += to_f32(q[(tok0 + rr) * ks + kh + c]) * ki;
-        }
-        if (qk.norm) {
-          sk *= nrm[rr] * nrm[ii];
-          sq *= nrm[C + rr] * nrm[ii];
-        }
-      }
-      akk[j] = sk;
-      aqk[j] = sq;
-    }
-  }
-
   static __device__ __forceinline__ int fac_sa(int a) { return a; }
   static __device__ __forceinline__ int fac_diag(int a) { return TT + a; }
   static __device__ __forceinline__ int fac_kg(int b) { return 2 * TT + b; }
@@ -350,16 +315,11 @@ struct ChunkLocal {
     return f;
   }
 
-  // Number of workgroup barriers run() executes (every thread must call it).
-  static constexpr int NBAR = 5 + (TT - 1);
-
   // The whole stage (every thread of the workgroup must call it).  `in` must
   // have been filled by prefetch() for this
   // (chunk, head); run() never waits on global memory otherwise.
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
-                             ChunkOut<TIO> out, const TIO* __restrict__ q,
-                             const TIO* __restrict__ k, const DecayIn<TIO>& dec, int n_heads,
-                             int h, QkIn qk) {
+                             ChunkOut<TIO> out, QkIn qk) {
     float* Gs = reinterpret_cast<float*>(lds + Gm::OFF_GS);
     float* As = reinterpret_cast<float*>(lds + Gm::OFF_AS);
     float* Ts = reinterpret_cast<float*>(lds + Gm::OFF_TS);
@@ -376,7 +336,7 @@ struct ChunkLocal {
     float* fac = reinterpret_cast<float*>(lds + Gm::OFF_FAC);  // [NFAC][D]
     float* s_beta = reinterpret_cast<float*>(lds + Gm::OFF_BETA);
     int* s_flag = reinterpret_cast<int*>(lds + Gm::OFF_FLAG);
-    float* s_nrm = reinterpret_cast<float*>(lds + Gm::OFF_NRM);
+    float* ex = reinterpret_cast<float*>(lds + Gm::OFF_EXACT);  // [TT][2][16][16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -399,11 +359,8 @@ struct ChunkLocal {
       const int x = tid + NT * m;
       uint4 kv = in.k[m], qv = in.q[m];
       if (qk.norm) {  // the VPR lanes holding a row reduce its sum of squares
-        const float fk = normalise_row(kv), fq = normalise_row(qv);
-        if (x < C * VPR && x % VPR == 0) {
-          s_nrm[x / VPR] = fk;
-          s_nrm[C + x / VPR] = fq;
-        }
+        normalise_row(kv);
+        normalise_row(qv);
       }
       if (x < C * VPR) {
         const int r = x / VPR, cv = x % VPR;
@@ -496,8 +453,54 @@ struct ChunkLocal {
     }
     __syncthreads();
 
-    // ---- phase 2: scaled operands Lk, Lq, Rn, beta k 2^G (transposed) ------
-    //      and the per-channel factor vectors
+    // ---- phase 2: per-channel factor vectors, exact diagonal tiles where a
+    //      block's decay span is too large to factor, then the scaled
+    //      operands Lk, Lq, Rn, beta k 2^G (transposed) -----------------------
+    for (int c = tid; c < D; c += NT) {
+      float rh[TT + 1];
+#pragma unroll
+      for (int a = 0; a <= TT; ++a) rh[a] = rho[a * D + c];
+      int big = 0;
+#pragma unroll
+      for (int a = 0; a < TT; ++a) {
+        fac[fac_sa(a) * D + c] = fast_exp2(rh[a]);
+        fac[fac_diag(a) * D + c] = fast_exp2(rh[a] - rh[a + 1]);
+        fac[fac_kg(a) * D + c] = fast_exp2(rh[TT] - rh[a + 1]);
+        if (rh[a] - rh[a + 1] > kSpanMax) big |= 1 << a;
+#pragma unroll
+        for (int b = 0; b + 2 <= a; ++b) fac[fac_far(a, b) * D + c] = fast_exp2(rh[a] - rh[b + 1]);
+      }
+      if (big) atomicOr(s_flag, big);
+    }
+    __syncthreads();
+    const int flag = *s_flag;  // blocks whose diagonal tile is summed exactly
+    if (flag) {
+      // entry (a, r, i), i <= r < 16 of block a: sum over channels of
+      // k[r] k[i] 2^(G[r] - G[i]) and q[r] k[i] 2^(G[r] - G[i]) from the staged
+      // rows (rows past the chunk are zeros); two lanes per entry, half the
+      // channels each
+      for (int e = tid; e < TT * 512; e += NT) {
+        const int half = e & 1, ent = e >> 1;
+        const int a = ent >> 8, r = (ent >> 4) & 15, i = ent & 15;
+        float sk = 0.f, sq = 0.f;
+        if (((flag >> a) & 1) && i <= r) {
+          const int rr = 16 * a + r, ii = 16 * a + i;
+          for (int c = half * (D / 2); c < (half + 1) * (D / 2); ++c) {
+            const float f = fast_exp2(Gs[rr * GS_LD + c] - Gs[ii * GS_LD + c]);
+            const float ki = to_f32(Lk[ii * KS_LD + c]) * f;
+            sk += to_f32(Lk[rr * KS_LD + c]) * ki;
+            sq += to_f32(Lq[rr * KS_LD + c]) * ki;
+          }
+        }
+        sk += __shfl_xor(sk, 1, 64);
+        sq += __shfl_xor(sq, 1, 64);
+        if (half == 0) {
+          ex[((a * 2 + 0) * 16 + r) * 16 + i] = sk;
+          ex[((a * 2 + 1) * 16 + r) * 16 + i] = sq;
+        }
+      }
+      __syncthreads();  // the staged k and q are replaced next
+    }
 #pragma unroll
     for (int m = 0; m < NGRP; ++m) {
       const int grp = tid + NT * m;
@@ -533,28 +536,11 @@ struct ChunkLocal {
         store_frag8(KBt + (c + 1) * TK_LD + r0, kb[1]);
       }
     }
-    for (int c = tid; c < D; c += NT) {
-      float rh[TT + 1];
-#pragma unroll
-      for (int a = 0; a <= TT; ++a) rh[a] = rho[a * D + c];
-      int big = 0;
-#pragma unroll
-      for (int a = 0; a < TT; ++a) {
-        fac[fac_sa(a) * D + c] = fast_exp2(rh[a]);
-        fac[fac_diag(a) * D + c] = fast_exp2(rh[a] - rh[a + 1]);
-        fac[fac_kg(a) * D + c] = fast_exp2(rh[TT] - rh[a + 1]);
-        if (rh[a] - rh[a + 1] > kSpanMax) big |= 1 << a;
-#pragma unroll
-        for (int b = 0; b + 2 <= a; ++b) fac[fac_far(a, b) * D + c] = fast_exp2(rh[a] - rh[b + 1]);
-      }
-      if (big) atomicOr(s_flag, big);
-    }
     __syncthreads();
 
     // ---- phase 3: decayed Gram tiles; Kg fragments; Gam -------------------
     {
       constexpr int NPAIR = TT * (TT + 1) / 2;
-      const int flag = *s_flag;
       for (int p = wave; p < NPAIR; p += NW) {
         int a = 0, b = p;
         while (b > a) {
@@ -563,7 +549,11 @@ struct ChunkLocal {
         }
         f32x4 akk = zero4(), aqk = zero4();
         if (a == b && (flag >> a) & 1) {
-          exact_diag_tile(a, akk, aqk, q, k, dec, in.ea, n_heads, h, in.tok0, in.len, qk, s_nrm);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            akk[j] = ex[((a * 2 + 0) * 16 + 4 * lg + j) * 16 + l16];
+            aqk[j] = ex[((a * 2 + 1) * 16 + 4 * lg + j) * 16 + l16];
+          }
         } else {
           const TIO* lkr = Lk + (16 * a + l16) * KS_LD;
           const TIO* lqr = Lq + (16 * a + l16) * KS_LD;
@@ -594,6 +584,11 @@ struct ChunkLocal {
       }
     }
     __syncthreads();
+    if (Gm::EXACT_IN_T && flag) {  // T held the exact tiles: its upper blocks must read 0
+      constexpr int NZ = C * TK_LD * (int)sizeof(TIO) / 16;
+      for (int x = tid; x < NZ; x += NT) reinterpret_cast<uint4*>(Tb)[x] = uint4{0, 0, 0, 0};
+      __syncthreads();
+    }
 
     // ---- phase 4: T = (I + A)^-1 ------------------------------------------
     // Diagonal 16x16 blocks in wave 0, lane 16a + r holding row r of block a:

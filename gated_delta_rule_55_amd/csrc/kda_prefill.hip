@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const int it = item(w);
     const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(
         blocks + ((size_t)(it % n_heads) * ntu + it / n_heads) * Gm::OUT_BYTES);
-    CL::run(lds, in, scale, out, q, k, dec, n_heads, it % n_heads, qk);
+    CL::run(lds, in, scale, out, qk);
     __syncthreads();  // the next item overwrites the LDS
   };
   typename CL::Inputs cur, nxt;

@@ -28,7 +28,7 @@ from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import Optional, Sequence
+from typing import Tuple, Optional, Sequence
 
 import numpy as np
 
@@ -163,10 +163,14 @@ def make_inputs(
     scale: Optional[float] = None,
     n_k_heads: Optional[int] = None,
     qk_prenorm: bool = True,
+    a_range: Tuple[float, float] = (-3.0, 0.0),
 ) -> KdaInputs:
     """Packed varlen batch with the recipe in the module docstring.
     n_k_heads: q/k heads (a divisor of H; default H).  qk_prenorm = False
-    leaves q and k unnormalised (for kernels that normalise them)."""
+    leaves q and k unnormalised (for kernels that normalise them).
+    a_range: the interval a_h is drawn from for the Kimi gate (the workloads'
+    U(-3, 0); U(1, 3) gives per-token log-decays of about -2 to -40, the strong
+    per-channel decay that takes the chunked path's exact diagonal tiles)."""
     dv = dk if dv is None else dv
     Hg = H if n_k_heads is None else int(n_k_heads)
     if Hg < 1 or H % Hg:
@@ -198,7 +202,7 @@ def make_inputs(
             b = np.zeros((H, dk))
             g = -_softplus(x)
         elif gate == "kimi":
-            a = _rng(seed, "a").uniform(-3.0, 0.0, size=(H,))
+            a = _rng(seed, "a").uniform(a_range[0], a_range[1], size=(H,))
             b = _rng(seed, "b").normal(0.0, 0.5, size=(H, dk))
             g = -np.exp(a)[None, :, None] * _softplus(x + b[None, :, :])
         else:

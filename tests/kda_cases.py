@@ -65,5 +65,39 @@ def oracle_prefill(inp: synth.KdaInputs, fused_gate: bool = False, qk_l2norm: bo
     return oracle.prefill(q, k, f["v"], g, f["beta"], f["h0"], f["cu_seqlens"], f["scale"])
 
 
+# Per-token bound on o: each (token, head) row's error against
+#   TOK_FACTOR x the whole-tensor bar x (|ref row| + 0.1 x rms of the ref rows),
+# so a single wrong token fails even when the whole-tensor rel-L2 of a long
+# sequence would hide it; the 0.1 rms floor keeps rows whose reference is
+# near zero from turning rounding noise into a large relative error.
+TOK_FACTOR = 10.0
+
+
+def token_errors(o, ref) -> np.ndarray:
+    """Per-row error ratio err / (|ref| + 0.1 rms) over the last axis."""
+    o = np.asarray(o, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.linalg.norm(o - ref, axis=-1)
+    rn = np.linalg.norm(ref, axis=-1)
+    rms = float(np.sqrt(np.mean(rn ** 2))) if rn.size else 0.0
+    return err / (rn + 0.1 * rms + 1e-300)
+
+
+def check_tokens(o, ref, tol: float) -> float:
+    """Assert the per-token bound; returns the worst row's ratio."""
+    if np.asarray(ref).size == 0:
+        return 0.0
+    worst = float(token_errors(o, ref).max())
+    assert worst <= TOK_FACTOR * tol, f"worst token row {worst:.3e} > {TOK_FACTOR * tol:.1e}"
+    return worst
+
+
+def worst_head(o, ref) -> float:
+    """Largest rel-L2 over the head axis (axis 1 of [T, H, d] or [N, H, d, d])."""
+    o = np.asarray(o, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return max(rel_l2(o[:, i], ref[:, i]) for i in range(ref.shape[1]))
+
+
 def say(msg: str):
     print(msg, flush=True)

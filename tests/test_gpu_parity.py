@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import synth
-from kda_cases import TOL, dev_inputs, oracle_prefill, rel_l2, say, to_host64
+from kda_cases import (TOL, check_tokens, dev_inputs, oracle_prefill, rel_l2, say, to_host64,
+                       worst_head)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +51,11 @@ def test_prefill_small(kda, dtype, d, chunk, lengths, h0):
     o, hT = run_prefill(kda, inp)
     o_ref, hT_ref = oracle_prefill(inp)
     eo, es = rel_l2(o, o_ref), rel_l2(hT, hT_ref)
-    say(f"  rel-L2 o={eo:.3e} state={es:.3e}")
-    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    who, whs = worst_head(o, o_ref), worst_head(hT, hT_ref)
+    tok = check_tokens(o, o_ref, TOL[dtype])
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e} worst head o={who:.3e} state={whs:.3e} "
+        f"worst token {tok:.3e}")
+    assert max(eo, es, who, whs) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 32), ("f32", 128), ("bf16", 64), ("bf16", 128)])
