@@ -43,6 +43,14 @@ class OracleLib:
         lib.kda_oracle_decode_f64.restype = ctypes.c_int
         lib.kda_oracle_num_threads.argtypes = []
         lib.kda_oracle_num_threads.restype = ctypes.c_int
+        # the fp32 twin (absent from the single-source builds the tests plant
+        # mistakes in)
+        self.has_f32 = hasattr(lib, "kda_oracle_prefill_f32")
+        if self.has_f32:
+            i64, fp = ctypes.c_int64, ctypes.POINTER(ctypes.c_float)
+            lib.kda_oracle_prefill_f32.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64), fp,
+                                                   fp, fp, fp, fp, fp, ctypes.c_float, fp, fp]
+            lib.kda_oracle_prefill_f32.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -78,6 +86,29 @@ class OracleLib:
         if rc != 0:
             raise RuntimeError(f"oracle prefill failed ({rc})")
         return o, ht
+
+    def prefill_f32(self, q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
+        """The fp32 twin of prefill(): the same token loop with every value and
+        every accumulation in fp32 (inputs rounded to fp32 first).  A
+        diagnostic of the fp32 floor; returns fp64 copies of the fp32 results."""
+        f32 = lambda x: np.ascontiguousarray(np.asarray(x, dtype=np.float32))  # noqa: E731
+        q, k, v, g, beta = f32(q), f32(k), f32(v), f32(g), f32(beta)
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        cu = np.array([0, T], dtype=np.int64) if cu_seqlens is None else \
+            np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = cu.shape[0] - 1
+        h0a = None if h0 is None else f32(h0)
+        sc = float(dk ** -0.5) if scale is None else float(scale)
+        o = np.zeros((T, H, dv), dtype=np.float32)
+        ht = np.zeros((N, H, dk, dv), dtype=np.float32)
+        fp = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))  # noqa: E731
+        rc = self.lib.kda_oracle_prefill_f32(
+            N, H, dk, dv, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), fp(q), fp(k), fp(v),
+            fp(g), fp(beta), fp(h0a), sc, fp(o), fp(ht))
+        if rc != 0:
+            raise RuntimeError(f"oracle fp32 prefill failed ({rc})")
+        return o.astype(np.float64), ht.astype(np.float64)
 
     def decode(self, state, q, k, v, g, beta, scale=None):
         """One decode step.  state: [N, H, dk, dv]; q, k, g: [N, H, dk]; v: [N, H, dv];
@@ -117,6 +148,10 @@ def prefill(*args, **kwargs):
 
 def decode(*args, **kwargs):
     return default().decode(*args, **kwargs)
+
+
+def prefill_f32(*args, **kwargs):
+    return default().prefill_f32(*args, **kwargs)
 
 
 def num_threads() -> int:
