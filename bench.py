@@ -193,6 +193,55 @@ def bench_prefill_batch(args, torch, kda, synth, cfg, full=None):
             "kernels_ms": {kname: round(v, 4) for kname, v in stage.items()}}
 
 
+def bench_prefill_4k(args, torch, kda, synth, reps=10):
+    """The prefill-4k workload (1 sequence x 4096 tokens, H=32, d=128, no h0):
+    warm, back to back (its 204 MB of inputs and outputs fit the 256 MB
+    Infinity Cache), and cold, each pass timed alone right after a 512 MB
+    scratch fill outside the timed region."""
+    log("generating the prefill-4k inputs (seeded numpy)")
+    inp = synth.make_config(1)
+    T, H, D = inp.T, inp.H, inp.dk
+    q, k, v = (to_dev(x, torch) for x in (inp.q, inp.k, inp.v))
+    beta, g = to_dev(inp.beta, torch), to_dev(inp.g, torch)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device="cuda")
+    ht = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.prefill_workspace_bytes(T, H, D, 1, 64), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    flush = _flusher(torch)
+
+    def run():
+        kda.chunk_prefill(q, k, v, g, beta, None, None, scale=inp.scale, chunk=64, out=o, ht=ht,
+                          workspace=ws)
+
+    def timed(pre=None):
+        if pre:
+            pre()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    warm = statistics.median([timed() for _ in range(reps)])
+    cold = statistics.median([timed(flush) for _ in range(reps)])
+    alg = T * BYTES_PER_TOKEN + STATE_BYTES
+    res = {"workload": "prefill-4k: 1 sequence x 4096 tokens, H=32, dk=dv=128, chunk 64, bf16 "
+                       "q/k/v/beta/o, fp32 g, no h0",
+           "warm": {"ms_per_pass": round(warm, 4), "tokens_per_s": round(T / (warm / 1e3), 1),
+                    "frac": round(alg / (warm / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "cold": {"ms_per_pass": round(cold, 4), "tokens_per_s": round(T / (cold / 1e3), 1),
+                    "frac": round(alg / (cold / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "note": f"{alg} algorithmic bytes per pass; each pass timed alone (HIP events around "
+                   f"the call), median of {reps}; cold passes follow a {FLUSH_BYTES >> 20} MB "
+                   "scratch fill, warm ones follow the previous pass"}
+    del q, k, v, beta, g, o, ws
+    return res
+
+
 def bench_decode(args, torch, kda, synth, inp):
     N, L, P, S = 64, 1280, 1024, args.decode_steps
     H, D = inp.H, inp.dk
@@ -210,52 +259,53 @@ def bench_decode(args, torch, kda, synth, inp):
     # the same steps on a bf16 copy of the state (half the state bytes)
     eager16, ms16 = _decode_steps_timed(args, torch, kda, inp, state0.to(torch.bfloat16), dec,
                                         out, stream)
+    cold = _decode_cold(torch, kda, inp, state0, dec, stream)
     rec = bench_recurrent(args, torch, kda, inp, state0, dec, stream)
     rec["eager_decode_ms_per_step"] = round(eager / S, 5)
     rec["bf16_state"] = {"ms": ms16, "eager_ms_per_step": round(eager16 / S, 5)}
-    return inp, S, ms, dec, rec
+    return inp, S, ms, dec, rec, state0, cold
 
 
-def _decode_steps_timed(args, torch, kda, inp, state0, dec, out, stream):
-    """S decode steps from state0: median eager time (one Python call per
-    step) and median time of the same steps replayed from a captured graph,
-    as a serving loop issues decode (the kernels' own time, without per-call
-    host cost).  Each replay is checked bit for bit against the eager run."""
-    S = out.shape[0]
+FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def _flusher(torch):
+    """A 512 MB buffer whose fill, issued between timed launches, leaves the
+    Infinity Cache holding only its own lines."""
+    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.fill_(1.0)
+    return flush
+
+
+def _decode_cold(torch, kda, inp, state0, dec, stream, n=32):
+    """Decode steps with the Infinity Cache flushed before each: n x (512 MB
+    scratch fill, step) back to back between two events, minus n fills alone,
+    divided by n -- each step then reads the state and its inputs from HBM.
+    The back-to-back steps of the main leg keep the 134 MB state in the
+    256 MB Infinity Cache instead."""
+    flush = _flusher(torch)
     state = state0.clone()
+    out = torch.empty((state.shape[0], inp.H, inp.dk), dtype=torch.bfloat16, device="cuda")
 
-    def steps():
-        for s in range(S):
-            kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
-                                 dec["beta"][s], scale=inp.scale, out=out[s])
-
-    def timed(fn):
-        state.copy_(state0)  # restore, untimed
-        torch.cuda.synchronize()
+    def span(with_step):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(stream)
-        fn()
+        for s in range(n):
+            flush()
+            if with_step:
+                kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
+                                     dec["beta"][s], scale=inp.scale, out=out)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b)
 
-    state.copy_(state0)
-    steps()  # warm-up
-    eager = [timed(steps) for _ in range(args.decode_reps)]
-    out_ref, state_ref = out.clone(), state.clone()
-    graph = torch.cuda.CUDAGraph()
-    state.copy_(state0)
-    torch.cuda.synchronize()
-    cap = torch.cuda.Stream()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            steps()
-    times = []
-    for _ in range(max(3, args.decode_reps)):
-        times.append(timed(graph.replay))
-        if not (torch.equal(state, state_ref) and torch.equal(out, out_ref)):
-            raise RuntimeError("graph replay of the decode steps differs from the eager run")
-    return statistics.median(eager), statistics.median(times)
+    span(True)  # warm-up
+    both = statistics.median([span(True) for _ in range(3)])
+    fills = statistics.median([span(False) for _ in range(3)])
+    return {"cold_ms": (both - fills) / n, "fill_ms": fills / n, "n": n}
 
 
 def bench_recurrent(args, torch, kda, inp, state0, dec, stream, R=16):
@@ -414,40 +464,100 @@ def bench_conv(args, torch, kda, T=32768, N_dec=64, reps=10, dec_calls=256):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_runs(fn, runs=3):
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), times
+
+
 def cpu_prefill_baseline(args, inp):
     """The fp64 oracle (C, OpenMP over the 32 head chains) on the prefill-32k
-    inputs: the whole sequence, repeated until about --cpu-seconds of CPU time
-    has passed (at least once), reported as tokens/s."""
+    inputs: all host threads over the whole sequence, median of 3 runs; and
+    one thread over a sample of the heads (the chains are independent and
+    equal in work, so tokens/s at 32 heads scales by the sampled fraction),
+    median of 3 runs."""
     import oracle
 
     f = inp.f64()
-    reps, total = 0, 0.0
-    while reps == 0 or total < args.cpu_seconds:
-        t0 = time.perf_counter()
-        oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"], None, f["scale"])
-        total += time.perf_counter() - t0
-        reps += 1
-    return {"value": reps * inp.T / total, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 token recurrence over all {inp.T} tokens x 32 heads of the "
-                      f"prefill-32k inputs (with h0), run {reps} times, {total:.1f} s in total"}
+    threads = oracle.num_threads()
+    med, runs = _median_runs(lambda: oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"],
+                                                    f["h0"], None, f["scale"]))
+    heads = [0, 11, 22]
+    sub = synth_slice(inp, heads).f64()
+    oracle.set_num_threads(1)
+    try:
+        med1, runs1 = _median_runs(lambda: oracle.prefill(sub["q"], sub["k"], sub["v"], sub["g"],
+                                                          sub["beta"], sub["h0"], None,
+                                                          sub["scale"]))
+    finally:
+        oracle.set_num_threads(threads)
+    frac = len(heads) / inp.H
+    return {"value": round(inp.T / med, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"fp64 token recurrence over all {inp.T} tokens x {inp.H} heads of the "
+                      f"prefill-32k inputs (with h0), {threads} threads, median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in runs)} s)",
+            "single_thread": {"value": round(inp.T * frac / med1, 1), "unit": "tokens/s",
+                              "cores": 1,
+                              "sample": f"heads {heads} of the same inputs, one thread, median of "
+                                        f"3 runs ({', '.join(f'{t:.2f}' for t in runs1)} s); "
+                                        f"tokens/s at {inp.H} heads = T x {len(heads)}/{inp.H} / "
+                                        "time"}}
 
 
-def cpu_decode_baseline(inp, dec, n_steps=8):
+def synth_slice(inp, heads):
+    import synth
+
+    return synth.slice_heads(inp, heads)
+
+
+def cpu_decode_baseline(inp, dec, state0, n_steps=32, n_steps_1t=4):
+    """The fp64 oracle's decode step at batch 64 from the carried decode-leg
+    state (the GPU's chunked prefill of 1024 tokens per sequence), all host
+    threads over n_steps steps and one thread over n_steps_1t steps, each the
+    median of 3 runs."""
     import numpy as np
 
     import oracle
 
-    N, H, D = 64, inp.H, inp.dk
-    st = np.zeros((N, H, D, D))
+    st0 = state0.double().cpu().numpy()
     arrs = {kk: t[:n_steps].float().cpu().numpy().astype(np.float64) for kk, t in dec.items()}
-    t0 = time.perf_counter()
-    for s in range(n_steps):
-        _, st = oracle.decode(st, arrs["q"][s], arrs["k"][s], arrs["v"][s], arrs["g"][s],
-                              arrs["beta"][s], inp.scale)
-    dt = time.perf_counter() - t0
-    return {"value": n_steps / dt, "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": f"{n_steps} fp64 decode steps at batch 64, H=32, d=128"}
+
+    def steps(n):
+        st = st0
+        for s in range(n):
+            _, st = oracle.decode(st, arrs["q"][s], arrs["k"][s], arrs["v"][s], arrs["g"][s],
+                                  arrs["beta"][s], inp.scale)
+
+    threads = oracle.num_threads()
+    med, runs = _median_runs(lambda: steps(n_steps))
+    oracle.set_num_threads(1)
+    try:
+        med1, runs1 = _median_runs(lambda: steps(n_steps_1t))
+    finally:
+        oracle.set_num_threads(threads)
+    return {"value": round(n_steps / med, 2), "unit": "steps/s", "cores": threads,
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"{n_steps} fp64 decode steps at batch 64, H=32, d=128 from the carried "
+                      f"state, {threads} threads, median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in runs)} s)",
+            "single_thread": {"value": round(n_steps_1t / med1, 3), "unit": "steps/s", "cores": 1,
+                              "sample": f"{n_steps_1t} steps, one thread, median of 3 runs "
+                                        f"({', '.join(f'{t:.2f}' for t in runs1)} s)"}}
 
 
 def main():
@@ -533,6 +643,8 @@ def main():
                          "scope": f"whole prefill pass, {gbytes} algorithmic bytes per pass"},
             "kernels_ms": {kname: round(v, 4) for kname, v in gstage.items()},
         }
+    if not args.no_batch:
+        line["prefill_4k"] = bench_prefill_4k(args, torch, kda, synth)
     inp4 = None
     if not (args.no_batch and args.no_decode):
         log("generating the decode-64x256 inputs (seeded numpy)")
@@ -541,7 +653,7 @@ def main():
         line["prefill_batches"] = [bench_prefill_batch(args, torch, kda, synth, 3),
                                    bench_prefill_batch(args, torch, kda, synth, 4, inp4)]
     if not args.no_decode:
-        dinp, S, dms, dec, rec = bench_decode(args, torch, kda, synth, inp4)
+        dinp, S, dms, dec, rec, dstate0, cold = bench_decode(args, torch, kda, synth, inp4)
         step_ms = dms / S
         dbytes = DECODE_STATE_BYTES + DECODE_TOKEN_BYTES
         dach = dbytes / (step_ms / 1e3) / 1e9
@@ -555,8 +667,17 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dach, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(dach / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode"),
-                         "note": "the 134 MB state fits the 256 MB Infinity Cache"},
+                         "note": "back-to-back steps: the 134 MB state stays in the 256 MB "
+                                 "Infinity Cache between steps, so this fraction includes "
+                                 "Infinity Cache hits; see cold"},
         }
+        cach = dbytes / (cold["cold_ms"] / 1e3) / 1e9
+        line["decode"]["cold"] = {
+            "ms_per_step": round(cold["cold_ms"], 5), "steps_per_s": round(1e3 / cold["cold_ms"], 1),
+            "frac": round(cach / HBM_PEAK_GBS, 4), "achieved": round(cach, 1),
+            "note": f"{cold['n']} x ({FLUSH_BYTES >> 20} MB scratch fill, step) back to back "
+                    f"minus {cold['n']} fills alone ({cold['fill_ms']:.4f} ms each), per step: "
+                    "each step reads the state and its inputs from HBM, not the Infinity Cache"}
         b16 = rec.pop("bf16_state")
         step16 = b16["ms"] / S
         bytes16 = DECODE_STATE_BYTES // 2 + DECODE_TOKEN_BYTES
@@ -581,7 +702,7 @@ def main():
     # the host thread that issues the GPU legs
     if not args.no_decode and not args.no_cpu:
         log("timing the CPU oracle (decode)")
-        line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec)
+        line["decode"]["cpu_baseline"] = cpu_decode_baseline(dinp, dec, dstate0)
     if not args.no_decode:
         del dec
     if args.copy_probe_mib:

@@ -16,7 +16,7 @@ SOURCES = ["kda_abi.cpp", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",
     # Packed-fp32 instructions are kept out of every kernel (the host pass
     # ignores the feature with a warning).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

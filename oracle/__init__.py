@@ -11,7 +11,8 @@ it.  Contents:
   conv.py                       short causal conv with carried taps (fp64)
   heads.py                      q/k L2 normalisation, grouped key heads (fp64)
 """
-from .recurrent import OracleLib, decode, lib_path, num_threads, prefill, prefill_f32  # noqa: F401
+from .recurrent import (OracleLib, decode, lib_path, num_threads, prefill,  # noqa: F401
+                        prefill_f32, set_num_threads)
 from .chunked import chunked_prefill, unit_lower_inverse  # noqa: F401
 from .gate import kimi_gate, softplus  # noqa: F401
 from .conv import causal_conv1d, silu  # noqa: F401

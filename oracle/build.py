@@ -23,6 +23,7 @@ def fp32_twin(src_text: str) -> str:
     t = re.sub(r"\bdouble\b", "float", src_text)
     t = re.sub(r"\bexp\(", "expf(", t)
     t = t.replace("_f64(", "_f32(").replace("kda_oracle_num_threads", "kda_oracle_num_threads_f32")
+    t = t.replace("kda_oracle_set_num_threads", "kda_oracle_set_num_threads_f32")
     return t
 
 

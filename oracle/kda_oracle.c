@@ -85,6 +85,15 @@ int kda_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads later calls use (n >= 1); no effect without OpenMP. */
+void kda_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Token-by-token prefill over packed sequences.
  * cu_seqlens: host array [n_seqs + 1], non-decreasing, cu[0] = 0.
  * h0 may be NULL (zero initial state); ht may be NULL (final state dropped).

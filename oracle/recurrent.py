@@ -57,6 +57,11 @@ class OracleLib:
     def num_threads(self) -> int:
         return int(self.lib.kda_oracle_num_threads())
 
+    def set_num_threads(self, n: int) -> None:
+        """Threads of later calls (OpenMP over the independent chains)."""
+        if hasattr(self.lib, "kda_oracle_set_num_threads"):
+            self.lib.kda_oracle_set_num_threads(ctypes.c_int(int(n)))
+
     def prefill(self, q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
         """Token-by-token KDA prefill in fp64.
 
@@ -156,3 +161,7 @@ def prefill_f32(*args, **kwargs):
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    default().set_num_threads(n)
