@@ -158,6 +158,8 @@ def lib():
                                               ctypes.c_size_t, ctypes.c_void_p,
                                               ctypes.POINTER(ctypes.c_void_p)]
         L.kda_chunk_prefill_timed.restype = ctypes.c_int
+        L.kda_chunk_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.c_void_p]
+        L.kda_chunk_prefill_noalloc.restype = ctypes.c_int
         L.kda_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.kda_workspace_status.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [ctypes.POINTER(DecodeDesc), ctypes.c_void_p]
@@ -232,6 +234,14 @@ def chunk_prefill_timed_raw(desc: PrefillDesc, workspace: int, workspace_bytes: 
         arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     return int(lib().kda_chunk_prefill_timed(ctypes.byref(desc), workspace, workspace_bytes,
                                              stream, arr))
+
+
+# Bytes of the static workspace kda_chunk_prefill_noalloc uses (one per device).
+KDA_NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
+def chunk_prefill_noalloc_raw(desc: PrefillDesc, stream: int) -> int:
+    return int(lib().kda_chunk_prefill_noalloc(ctypes.byref(desc), stream))
 
 
 def recurrent_decode_raw(desc: DecodeDesc, stream: int) -> int:

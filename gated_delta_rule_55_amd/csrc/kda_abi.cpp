@@ -346,6 +346,21 @@ int kda_chunk_prefill(const kda_prefill_desc* d, void* workspace, size_t workspa
   return kda_chunk_prefill_timed(d, workspace, workspace_bytes, stream, nullptr);
 }
 
+int kda_chunk_prefill_noalloc(const kda_prefill_desc* d, void* stream) {
+  kda::PrefillArgs a;
+  int st = check_prefill(d, &a);
+  if (st != KDA_OK) return st;
+  Range rin[10];
+  st = check_prefill_pointers(d, &a, rin);
+  if (st != KDA_OK) return st;
+  static_assert(kda::kNoAllocWorkspaceBytes == KDA_NOALLOC_WORKSPACE_BYTES, "header limit");
+  if (kda::prefill_workspace_bytes(a) > kda::kNoAllocWorkspaceBytes) return KDA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = kda::noalloc_workspace(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(kda::launch_prefill(a, ws, (hipStream_t)stream, nullptr));
+}
+
 int kda_recurrent_prefill(const kda_prefill_desc* d, void* stream) {
   kda::PrefillArgs a;
   int st = check_prefill(d, &a, false);

@@ -115,4 +115,11 @@ hipError_t launch_conv_update(const ConvArgs& a, hipStream_t stream);
 // Offset of the device status word inside a prefill workspace.
 constexpr size_t kWsStatusOffset = 0;
 
+// The no-allocation prefill's workspace: a static device array of this many
+// bytes (KDA_NOALLOC_WORKSPACE_BYTES), one per device, held until the process
+// ends.  *ptr receives its address on the current device (looked up once per
+// device with hipGetSymbolAddress).
+constexpr size_t kNoAllocWorkspaceBytes = (size_t)64 << 20;
+hipError_t noalloc_workspace(void** ptr);
+
 }  // namespace kda

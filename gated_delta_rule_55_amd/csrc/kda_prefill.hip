@@ -10,10 +10,41 @@
 // launches: the chunk map (varlen chunk table from the device cu_seqlens), the
 // chunk-local stage over every (chunk, head) into a workspace, and the state
 // scan with the output fused in, which reads the workspace back.
+#include <mutex>
+
 #include "kda_chunk_ops.h"
 #include "kda_launch.h"
 
 namespace kda {
+
+// Workspace of the no-allocation entry point (kda_chunk_prefill_noalloc):
+// every device the library runs on holds its own copy until the process ends.
+// Host code never uses this name as an address: it takes the device address
+// from hipGetSymbolAddress (noalloc_workspace below).
+static __device__ __align__(256) unsigned char scratch[kNoAllocWorkspaceBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+}  // namespace
+
+hipError_t noalloc_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {  // first use on this device, which is current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

@@ -150,7 +150,7 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   output_final_state: bool = True, stream=None, events=None,
                   plan: str = "auto", gate=None,
                   state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-                  state_dtype: Optional[torch.dtype] = None
+                  state_dtype: Optional[torch.dtype] = None, noalloc: bool = False
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k: [T, Hg, dk] (Hg key heads, each shared by
     H / Hg consecutive value heads; Hg = H by default); g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
@@ -169,12 +169,23 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     `qk_l2norm`: L2-normalise every q and k row in the kernels (eps 1e-6).
     States (h0, ht) are fp32, or bf16 with bf16 inputs: their dtype is that of
     h0 / ht when given, else `state_dtype` (fp32 by default) for a new ht.  The
-    arithmetic is fp32 either way; a bf16 ht is rounded once when written."""
+    arithmetic is fp32 either way; a bf16 ht is rounded once when written.
+    `noalloc`: call kda_chunk_prefill_noalloc, whose workspace is the library's
+    static per-device buffer (KDA_NOALLOC_WORKSPACE_BYTES) -- nothing is
+    allocated for it; `workspace` and `events` must then be None, and `out`
+    (and `ht`) should be passed by callers that allocate nothing at all."""
     dev = q.device
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
                                         output_final_state, gate, state_indices, state_dtype)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate,
                         state_indices, n_slots, qk_l2norm)
+    if noalloc:
+        if workspace is not None or events is not None:
+            raise ValueError("noalloc takes no workspace and no events")
+        st = _abi.chunk_prefill_noalloc_raw(desc, _stream(stream))
+        if st != _abi.KDA_OK:
+            raise _abi.KdaError(st, "kda_chunk_prefill_noalloc")
+        return out, ht
     need = _abi.workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -240,6 +240,25 @@ int kda_chunk_prefill_timed(const kda_prefill_desc* d, void* workspace, size_t w
  * Returns KDA_ERR_HIP if the copy fails. */
 int kda_workspace_status(const void* workspace, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kda_chunk_prefill with its workspace taken from a buffer of
+ * KDA_NOALLOC_WORKSPACE_BYTES that the library holds in static device memory,
+ * one per device, until the process ends (its address is looked up on the
+ * first call on each device).  The call allocates nothing; the caller passes
+ * every input and output as for kda_chunk_prefill.  Returns
+ * KDA_ERR_WORKSPACE, before anything is enqueued, when
+ * kda_chunk_prefill_workspace_bytes(d) exceeds the buffer (64 MiB: at H = 32,
+ * dk = dv = 128, chunk 64 that is t_total / 64 + n_seqs <= 25 chunks, one
+ * sequence of up to 1,536 tokens).  Every call on a device shares that device's buffer and
+ * leaves its contents behind: calls on one stream are ordered, but calls that
+ * overlap on one device (other streams, other threads) race and must not be
+ * issued.  The device status word that kda_workspace_status reads for the
+ * other entry point lives in this buffer and is not exposed: invalid
+ * cu_seqlens contents write no o and no ht, unreported. */
+#define KDA_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+int kda_chunk_prefill_noalloc(const kda_prefill_desc* d, void* stream);
+
 /* Enqueue one recurrent decode step on `stream`.  Returns a kda_status. */
 int kda_recurrent_decode(const kda_decode_desc* d, void* stream);
 

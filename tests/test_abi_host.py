@@ -321,3 +321,20 @@ def test_state_dtype_validation(abi):
                                     0) == abi.KDA_ERR_ALIAS
     assert abi.recurrent_decode_raw(abi.decode_desc(**dict(kw, o=o), **pool, state_dtype=BF16),
                                     0) == abi.KDA_ERR_HIP
+
+
+@no_gpu_only
+def test_noalloc_rejects_oversize_before_launch(abi):
+    """The no-allocation entry point refuses a call whose workspace would not
+    fit its static buffer (64 MiB), on the host; 1,536 tokens at 32 heads fit,
+    1,600 do not."""
+    L = abi.lib()
+    far = dict(q=0x10000000, k=0x20000000, v=0x30000000, g=0x40000000, beta=0x50000000,
+               o=0x60000000)  # made-up addresses far enough apart not to alias
+    big = _valid_prefill(abi, t_total=1600, n_heads=32, **far)
+    assert abi.workspace_bytes(big) > abi.KDA_NOALLOC_WORKSPACE_BYTES
+    assert L.kda_chunk_prefill_noalloc(ctypes.byref(big), None) == abi.KDA_ERR_WORKSPACE
+    ok = _valid_prefill(abi, t_total=1536, n_heads=32, **far)
+    assert abi.workspace_bytes(ok) <= abi.KDA_NOALLOC_WORKSPACE_BYTES
+    bad = _valid_prefill(abi, t_total=1536, n_heads=32, dtype=7, **far)
+    assert L.kda_chunk_prefill_noalloc(ctypes.byref(bad), None) == abi.KDA_ERR_DTYPE
