@@ -266,6 +266,48 @@ def bench_decode(args, torch, kda, synth, inp):
     return inp, S, ms, dec, rec, state0, cold
 
 
+def _decode_steps_timed(args, torch, kda, inp, state0, dec, out, stream):
+    """S decode steps from state0: median eager time (one Python call per
+    step) and median time of the same steps replayed from a captured graph,
+    as a serving loop issues decode (the kernels' own time, without per-call
+    host cost).  Each replay is checked bit for bit against the eager run."""
+    S = out.shape[0]
+    state = state0.clone()
+
+    def steps():
+        for s in range(S):
+            kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
+                                 dec["beta"][s], scale=inp.scale, out=out[s])
+
+    def timed(fn):
+        state.copy_(state0)  # restore, untimed
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    state.copy_(state0)
+    steps()  # warm-up
+    eager = [timed(steps) for _ in range(args.decode_reps)]
+    out_ref, state_ref = out.clone(), state.clone()
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            steps()
+    times = []
+    for _ in range(max(3, args.decode_reps)):
+        times.append(timed(graph.replay))
+        if not (torch.equal(state, state_ref) and torch.equal(out, out_ref)):
+            raise RuntimeError("graph replay of the decode steps differs from the eager run")
+    return statistics.median(eager), statistics.median(times)
+
+
 FLUSH_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
 
 

@@ -315,11 +315,49 @@ struct ChunkLocal {
     return f;
   }
 
+  // Take delivery of every load prefetch() issued into `in` (emits only the
+  // wait).  Memory counters retire in order and count stores too, so a
+  // prefetch waited for after the previous item's stores would also wait for
+  // those stores; settling it before they are issued avoids that.
+  template <typename T>
+  static __device__ __forceinline__ void touch(T& x) {
+    using R = unsigned __attribute__((ext_vector_type(sizeof(T) / 4)));
+    static_assert(sizeof(T) % 4 == 0 && sizeof(T) >= 8, "register group");
+    R r = __builtin_bit_cast(R, x);
+    asm volatile("" : "+v"(r));
+    x = __builtin_bit_cast(T, r);
+  }
+  static __device__ __forceinline__ void settle(Inputs& in) {
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      touch(in.k[m]);
+      touch(in.q[m]);
+      touch(in.v[m]);
+    }
+    if constexpr (GATE) {
+#pragma unroll
+      for (int m = 0; m < NG; ++m) {
+        touch(in.x[m]);
+        touch(in.bias[m]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NG; ++m) touch(in.g[m]);
+    }
+    using B = std::conditional_t<sizeof(TIO) == 2, unsigned short, unsigned>;
+    B b = __builtin_bit_cast(B, in.beta);
+    asm volatile("" : "+v"(b));
+    in.beta = __builtin_bit_cast(TIO, b);
+  }
+
   // The whole stage (every thread of the workgroup must call it).  `in` must
-  // have been filled by prefetch() for this
-  // (chunk, head); run() never waits on global memory otherwise.
+  // have been filled by prefetch() for this (chunk, head) and settled; run()
+  // never waits on global memory otherwise.  mid() runs after the Gram
+  // tiles, before the first output store (the caller settles the next item's
+  // prefetch there).
+  template <typename Mid>
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
-                             ChunkOut<TIO> out, QkIn qk) {
+                             ChunkOut<TIO> out, QkIn qk, Mid&& mid) {
     float* Gs = reinterpret_cast<float*>(lds + Gm::OFF_GS);
     float* As = reinterpret_cast<float*>(lds + Gm::OFF_AS);
     float* Ts = reinterpret_cast<float*>(lds + Gm::OFF_TS);
@@ -589,6 +627,8 @@ struct ChunkLocal {
       for (int x = tid; x < NZ; x += NT) reinterpret_cast<uint4*>(Tb)[x] = uint4{0, 0, 0, 0};
       __syncthreads();
     }
+
+    mid();
 
     // ---- phase 4: T = (I + A)^-1 ------------------------------------------
     // Diagonal 16x16 blocks in wave 0, lane 16a + r holding row r of block a:

@@ -173,20 +173,24 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const ChunkEnt ent = tab[it / n_heads];
     CL::prefetch(in, q, k, v, dec, beta, n_heads, it % n_heads, ent.start, ent.len, qk);
   };
+  typename CL::Inputs cur, nxt;
   auto compute = [&](const typename CL::Inputs& in, int w) {
     const int it = item(w);
     const ChunkOut<TIO> out = chunk_out_at<TIO, D, C>(
         blocks + ((size_t)(it % n_heads) * ntu + it / n_heads) * Gm::OUT_BYTES);
-    CL::run(lds, in, scale, out, qk);
+    CL::run(lds, in, scale, out, qk, [&] { CL::settle(nxt); });
     __syncthreads();  // the next item overwrites the LDS
   };
-  typename CL::Inputs cur, nxt;
   int w = blockIdx.x;
-  if (w < n_items) fetch(cur, w);
+  if (w < n_items) {
+    fetch(cur, w);
+    CL::settle(cur);
+  }
   while (w < n_items) {
     const int w2 = w + gridDim.x;
     // in flight during this item (past the end: the last item again, unused),
-    // issued unconditionally so the compiler's load counts stay exact
+    // issued unconditionally so the compiler's load counts stay exact, and
+    // settled midway through it, before its output stores
     fetch(nxt, w2 < n_items ? w2 : n_items - 1);
     compute(cur, w);
     cur = nxt;
@@ -222,8 +226,23 @@ int scan_tiles(int n_seqs, int n_heads, int cus) {
   }
   return 1;
 }
+// L2 warming: with WARM > 0 the workgroup has one more wave, which computes
+// nothing.  WARM chunks ahead of the step the other waves compute, it touches
+// one word of every 128-byte line of that chunk's block whose index is jb
+// (mod NB), so the NB workgroups of a head bring the whole block into their
+// XCD's L2 before their own loads ask for it.  It meets the other waves at
+// their barriers (the same count), which keeps it WARM chunks ahead and no
+// further, and consumes each load's value three steps after issuing it, so it
+// never waits for memory before a barrier.
 template <typename TIO, int D, int C, int NJ>
-__global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
+struct ScanWarm {
+  static constexpr int NB = (D / 16) / NJ;
+  static constexpr int LINES = (int)(Geo<TIO, D, C>::OUT_BYTES / 128);
+  static constexpr int NL = (LINES + NB * 64 - 1) / (NB * 64);  // loads per lane per chunk
+};
+
+template <typename TIO, int D, int C, int NJ, int WARM>
+__global__ __launch_bounds__(64 * (D / 32) + (WARM ? 64 : 0)) void state_scan_kernel(
     const void* __restrict__ h0, void* __restrict__ ht, TIO* __restrict__ o, int n_seqs,
     int n_heads, const int* __restrict__ status, const int* __restrict__ chunk_off,
     const ChunkEnt* __restrict__ tab, unsigned char* __restrict__ blocks, int ntu,
@@ -253,6 +272,42 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
     if (slot < 0 || slot >= n_slots) return;
   }
   SS::clear_vt(lds);
+  constexpr int NTH = 64 * (D / 32);  // threads of the computing waves
+  if (WARM && (int)threadIdx.x >= NTH) {
+    using SW = ScanWarm<TIO, D, C, NJ>;
+    const int c_begin = chunk_off[n], c_end = chunk_off[n + 1];
+    auto warm = [&](int ci, int (&r)[SW::NL]) {
+      ci = ci < c_end ? ci : c_end - 1;
+      const __amdgpu_buffer_rsrc_t rr =
+          make_rsrc(blocks + ((size_t)h * ntu + ci) * Gm::OUT_BYTES, (int)Gm::OUT_BYTES);
+#pragma unroll
+      for (int i = 0; i < SW::NL; ++i)
+        r[i] = __builtin_amdgcn_raw_buffer_load_b32(rr, (jb + NB * (lane + 64 * i)) * 128, 0, 0);
+    };
+    int ring[3][SW::NL];
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int i = 0; i < SW::NL; ++i) ring[u][i] = 0;
+    int acc = 0;
+    __syncthreads();
+    for (int ci = c_begin; ci < c_end; ci += 3) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+#pragma unroll
+        for (int i = 0; i < SW::NL; ++i) acc ^= ring[u][i];
+        warm(ci + u + WARM, ring[u]);
+        __syncthreads();  // the two barriers of a step
+        __syncthreads();
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int i = 0; i < SW::NL; ++i) acc ^= ring[u][i];
+    asm volatile("" ::"v"(acc));  // keeps the warming loads
+    return;
+  }
   f32x4 S[NJ][2];
   const size_t sbase = ((size_t)slot * n_heads + h) * D * D;
   // no h0: an empty buffer, whose loads read 0 (branch-free, so the compiler
@@ -296,7 +351,6 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   // counts stay exact.  Three chunks of operators are in flight: each buffer
   // keeps its role across the unrolled loop, and a step refills its buffer
   // with the chunk three ahead piece by piece as it consumes it.
-  constexpr int NTH = 64 * (D / 32);
   typename SS::Ops b0, b1, b2;
   auto clamp = [&](int ci) { return ci < c_end ? ci : c_end - 1; };
   auto fetch = [&](typename SS::Ops& buf, int ci) {
@@ -346,19 +400,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void state_scan_kernel(
   }
 }
 
+// Chunks of lookahead of the L2-warming wave (0: no warming wave).
+constexpr int kScanWarm = 4;
+
 template <typename TIO, int D, int C, int NJ>
 hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk_off,
                        const ChunkEnt* tab, unsigned char* blocks, int ntu, hipStream_t stream) {
   using SS = ScanStep<TIO, D, C, NJ>;
+  // The warming wave halves the registers each wave may hold (five waves on
+  // four SIMDs): only the one-tile bf16 scan leaves room for it.
+  constexpr int WARM = (sizeof(TIO) == 2 && NJ == 1) ? kScanWarm : 0;
   static_assert(SS::LDS_BYTES <= 160 * 1024, "scan LDS");
-  hipError_t err = hipFuncSetAttribute((const void*)state_scan_kernel<TIO, D, C, NJ>,
+  hipError_t err = hipFuncSetAttribute((const void*)state_scan_kernel<TIO, D, C, NJ, WARM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)SS::LDS_BYTES);
   if (err != hipSuccess) return err;
   const unsigned nblk = (unsigned)((int64_t)a.n_seqs * a.n_heads * SS::NB);
-  hipLaunchKernelGGL((state_scan_kernel<TIO, D, C, NJ>), dim3(nblk), dim3(64 * (D / 32)),
-                     SS::LDS_BYTES, stream, a.h0, a.ht, (TIO*)a.o, a.n_seqs, a.n_heads, status,
-                     chunk_off, tab, blocks, ntu, a.slots, a.n_slots, (int)a.state_bf16);
+  hipLaunchKernelGGL((state_scan_kernel<TIO, D, C, NJ, WARM>), dim3(nblk),
+                     dim3(64 * (D / 32) + (WARM ? 64 : 0)), SS::LDS_BYTES, stream, a.h0, a.ht,
+                     (TIO*)a.o, a.n_seqs, a.n_heads, status, chunk_off, tab, blocks, ntu, a.slots,
+                     a.n_slots, (int)a.state_bf16);
   return hipGetLastError();
 }
 
