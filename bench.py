@@ -328,6 +328,7 @@ def _decode_cold(torch, kda, inp, state0, dec, stream, n=32):
     The back-to-back steps of the main leg keep the 134 MB state in the
     256 MB Infinity Cache instead."""
     flush = _flusher(torch)
+    S = next(iter(dec.values())).shape[0]
     state = state0.clone()
     out = torch.empty((state.shape[0], inp.H, inp.dk), dtype=torch.bfloat16, device="cuda")
 
@@ -335,9 +336,10 @@ def _decode_cold(torch, kda, inp, state0, dec, stream, n=32):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record(stream)
-        for s in range(n):
+        for i in range(n):
             flush()
-            if with_step:
+            if with_step:  # the drawn decode tokens in turn, again from the first if n > S
+                s = i % S
                 kda.recurrent_decode(state, dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s],
                                      dec["beta"][s], scale=inp.scale, out=out)
         b.record(stream)

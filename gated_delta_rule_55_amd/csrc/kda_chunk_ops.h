@@ -353,8 +353,8 @@ struct ChunkLocal {
   // The whole stage (every thread of the workgroup must call it).  `in` must
   // have been filled by prefetch() for this (chunk, head) and settled; run()
   // never waits on global memory otherwise.  mid() runs after the Gram
-  // tiles, before the first output store (the caller settles the next item's
-  // prefetch there).
+  // tile pairs, before the first output store (the caller settles the next
+  // item's prefetch there).
   template <typename Mid>
   static __device__ void run(unsigned char* lds, const Inputs& in, float scale,
                              ChunkOut<TIO> out, QkIn qk, Mid&& mid) {
@@ -577,8 +577,11 @@ struct ChunkLocal {
     __syncthreads();
 
     // ---- phase 3: decayed Gram tiles; Kg fragments; Gam -------------------
+    // The waves with one Gram tile pair fewer than the rest write Kg and Gam
+    // to the outputs meanwhile (they read only Rn and the factors).
     {
       constexpr int NPAIR = TT * (TT + 1) / 2;
+      constexpr int KGW = (NPAIR % NW == 0) ? 0 : NPAIR % NW;  // first Kg wave
       for (int p = wave; p < NPAIR; p += NW) {
         int a = 0, b = p;
         while (b > a) {
@@ -620,6 +623,32 @@ struct ChunkLocal {
           Aq[rr * TK_LD + ii] = from_f32<TIO>((ii <= rr) ? aqk[j] : 0.f);
         }
       }
+      mid();  // before this item's first store
+      if (wave >= KGW) {
+        constexpr int NTK = NT - 64 * KGW;  // threads writing Kg
+        const int tk = tid - 64 * KGW;
+        // Kg^T fragments in kperm token order: element (kt, ts, lane, e) =
+        // Kg[32ts + kperm(lg, e)][16kt + l16], Kg = Rn * 2^(rho_TT - rho_{blk+1}).
+        for (int slot = tk; slot < DT * KBC * 64; slot += NTK) {
+          const int ln = slot & 63;
+          const int kt = (slot >> 6) / KBC, ts = (slot >> 6) % KBC;
+          const int c = 16 * kt + (ln & 15);
+          const int g4 = ln >> 4;
+          FragT f;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int blk = 2 * ts + hh;  // 16-token block of these four tokens
+            const float fk = (blk < TT) ? fac[fac_kg(blk < TT ? blk : 0) * D + c] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int tok = 16 * blk + 4 * g4 + e;
+              f[4 * hh + e] = from_f32<TIO>((blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fk : 0.f);
+            }
+          }
+          store_frag8(out.k + (size_t)slot * 8, f);
+        }
+        for (int c = tk; c < D; c += NTK) out.gam[c] = fast_exp2(rho[TT * D + c]);
+      }
     }
     __syncthreads();
     if (Gm::EXACT_IN_T && flag) {  // T held the exact tiles: its upper blocks must read 0
@@ -628,18 +657,20 @@ struct ChunkLocal {
       __syncthreads();
     }
 
-    mid();
-
     // ---- phase 4: T = (I + A)^-1 ------------------------------------------
-    // Diagonal 16x16 blocks in wave 0, lane 16a + r holding row r of block a:
-    // column-oriented substitution, row i of the inverse reaching the rows
-    // below it by a row broadcast; then the off-diagonal blocks one band at
-    // a time, one wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
-    // (fp32 MFMA).  Meanwhile the other waves write the Kg^T fragments and Gam.
-    if (wave == 0) {
+    // Diagonal 16x16 blocks by forward substitution, lane 16a + r holding row
+    // r of block a: the multiple A[r][i] of row i of the inverse, reaching the
+    // lanes below it by a row broadcast, is subtracted for i = 0 .. 14 in
+    // turn.  Columns of the inverse do not interact, so waves 0..3 each take
+    // the columns j = wave (mod 4); a row i < j still holds 0 in column j, so
+    // the steps before j are skipped.  Then the off-diagonal blocks one band
+    // at a time, one wave per block:  T_ab = -T_aa sum_{c=b}^{a-1} A_ac T_cb
+    // (fp32 MFMA).
+    auto diag_cols = [&](auto kc) {
+      constexpr int K = decltype(kc)::value;
       const int a = lg < TT ? lg : TT - 1;  // rows past the blocks: a copy, unused
       const int r = l16;
-      float Ar[16], X[16];
+      float Ar[16], X[4];
       const float* arow = As + (16 * a + r) * AF_LD + 16 * a;
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
@@ -648,46 +679,31 @@ struct ChunkLocal {
         for (int e = 0; e < 4; ++e) Ar[4 * j4 + e] = x4[e];
       }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) X[j] = (j == r) ? 1.f : 0.f;
+      for (int q = 0; q < 4; ++q) X[q] = (K + 4 * q == r) ? 1.f : 0.f;
       // A is strictly lower triangular: rows r <= i see a zero multiplier
 #pragma unroll
       for (int i = 0; i < 15; ++i) {
         const float m = -Ar[i];
 #pragma unroll
-        for (int j = 0; j <= i; ++j) X[j] = fmaf(m, row_bcast(X[j], i), X[j]);
+        for (int q = 0; q < 4; ++q)
+          if (K + 4 * q <= i) X[q] = fmaf(m, row_bcast(X[q], i), X[q]);
       }
       if (lg < TT) {
         float* trow = Ts + (16 * a + r) * AF_LD + 16 * a;
         TIO* brow = Tb + (16 * a + r) * TK_LD + 16 * a;
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4)
-          *reinterpret_cast<f32x4*>(trow + 4 * j4) =
-              f32x4{X[4 * j4], X[4 * j4 + 1], X[4 * j4 + 2], X[4 * j4 + 3]};
-#pragma unroll
-        for (int j = 0; j < 16; ++j) brow[j] = from_f32<TIO>(X[j]);
-      }
-    } else {
-      // Kg^T fragments in kperm token order: element (kt, ts, lane, e) =
-      // Kg[32ts + kperm(lg, e)][16kt + l16], Kg = Rn * 2^(rho_TT - rho_{blk+1}).
-      for (int slot = tid - 64; slot < DT * KBC * 64; slot += NT - 64) {
-        const int ln = slot & 63;
-        const int kt = (slot >> 6) / KBC, ts = (slot >> 6) % KBC;
-        const int c = 16 * kt + (ln & 15);
-        const int g4 = ln >> 4;
-        FragT f;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int blk = 2 * ts + hh;  // 16-token block of these four tokens
-          const float fk = (blk < TT) ? fac[fac_kg(blk < TT ? blk : 0) * D + c] : 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = 16 * blk + 4 * g4 + e;
-            f[4 * hh + e] = from_f32<TIO>((blk < TT) ? to_f32(Rn[tok * KS_LD + c]) * fk : 0.f);
-          }
+        for (int q = 0; q < 4; ++q) {
+          trow[K + 4 * q] = X[q];
+          brow[K + 4 * q] = from_f32<TIO>(X[q]);
         }
-        store_frag8(out.k + (size_t)slot * 8, f);
       }
-      for (int c = tid - 64; c < D; c += NT - 64) out.gam[c] = fast_exp2(rho[TT * D + c]);
+    };
+    switch (wave) {
+      case 0: diag_cols(std::integral_constant<int, 0>{}); break;
+      case 1: diag_cols(std::integral_constant<int, 1>{}); break;
+      case 2: diag_cols(std::integral_constant<int, 2>{}); break;
+      case 3: diag_cols(std::integral_constant<int, 3>{}); break;
+      default: break;
     }
     __syncthreads();
 #pragma unroll
@@ -907,12 +923,44 @@ struct ScanStep {
   // then overlap the rest of the step); nxt_ent supplies the new token range.
   // live = false (uniform) runs the step without effect: no o rows are
   // written and S keeps its value; the refills still happen.
-  template <int NTH>
+  // The chunk's rows of o from the staging buffer to HBM, by NTS threads
+  // (index tid): rows >= len fall outside the buffer resource; 16-byte
+  // pieces, EPV values of one row each.  Runs between the two barriers of the
+  // step that staged them.
+  template <int NTS>
+  static __device__ __forceinline__ void store_o(unsigned char* lds, TIO* __restrict__ o,
+                                                 int64_t ostride, int h, int jb, int start,
+                                                 int len, int tid) {
+    const TIO* Os = reinterpret_cast<const TIO*>(lds + OFF_OS);
+    constexpr int EPV = 16 / (int)sizeof(TIO), VPRO = 16 * NJ / EPV, NVEC = C * VPRO;
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
+#pragma unroll
+    for (int p = 0; p < (NVEC + NTS - 1) / NTS; ++p) {
+      const int x0 = tid + NTS * p;
+      const int x = x0 < NVEC ? x0 : NVEC - 1;
+      const int r = x / VPRO, cv = x % VPRO;
+      const uint4 val = *reinterpret_cast<const uint4*>(Os + r * OS_LD + cv * EPV);
+      const int off = (x0 < NVEC && r < len)
+                          ? (r * (int)ostride + h * D + 16 * NJ * jb + cv * EPV) * (int)sizeof(TIO)
+                          : kBufferOff;
+      buffer_store16(val, orsrc, off);
+    }
+  }
+
+  // STORE_O: the step's own waves write o (else another wave of the
+  // workgroup calls store_o between the step's barriers).
+  template <int NTH, bool STORE_O = true>
   static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[NJ][2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
                                               int jb, const ChunkOut<TIO>* nxt = nullptr,
                                               const ChunkEnt* nxt_ent = nullptr,
                                               bool live = true) {
+    // No instruction crosses a step boundary: the scheduler would otherwise
+    // hoist the next steps' conversions of their U and Ol values (loaded one
+    // and two steps ago) into this step, whose waits for them then hold up
+    // this step's chain.
+    __builtin_amdgcn_sched_barrier(0);
     const int start = __builtin_amdgcn_readfirstlane(op.start);
     const int len = live ? __builtin_amdgcn_readfirstlane(op.len) : 0;
     const FragT* Sx = reinterpret_cast<const FragT*>(lds);  // [NJ][KBD][64]
@@ -953,24 +1001,7 @@ struct ScanStep {
       load_uo(op, *nxt, jb);
     }
     __syncthreads();
-    {
-      // the chunk's rows of o as one raw buffer: rows >= len fall outside it;
-      // 16-byte pieces, EPV values of one row each
-      constexpr int EPV = 16 / (int)sizeof(TIO), VPRO = 16 * NJ / EPV, NVEC = C * VPRO;
-      const __amdgpu_buffer_rsrc_t orsrc =
-          make_rsrc(o + (int64_t)start * ostride, len * (int)ostride * (int)sizeof(TIO));
-#pragma unroll
-      for (int p = 0; p < (NVEC + NTH - 1) / NTH; ++p) {
-        const int x0 = (int)threadIdx.x + NTH * p;
-        const int x = x0 < NVEC ? x0 : NVEC - 1;
-        const int r = x / VPRO, cv = x % VPRO;
-        const uint4 val = *reinterpret_cast<const uint4*>(Os + r * OS_LD + cv * EPV);
-        const int off = (x0 < NVEC && r < len)
-                            ? (r * (int)ostride + h * D + 16 * NJ * jb + cv * EPV) * (int)sizeof(TIO)
-                            : kBufferOff;
-        buffer_store16(val, orsrc, off);
-      }
-    }
+    if constexpr (STORE_O) store_o<NTH>(lds, o, ostride, h, jb, start, len, (int)threadIdx.x);
     {
 #pragma unroll
       for (int c = 0; c < NJ; ++c)

@@ -227,8 +227,10 @@ int scan_tiles(int n_seqs, int n_heads, int cus) {
   return 1;
 }
 // L2 warming: with WARM > 0 the workgroup has one more wave, which computes
-// nothing.  WARM chunks ahead of the step the other waves compute, it touches
-// one word of every 128-byte line of that chunk's block whose index is jb
+// nothing; it writes each step's o from the staging buffer (between the
+// step's two barriers, off the chain of steps), and WARM chunks ahead of the
+// step the other waves compute, it touches one word of every 128-byte line of
+// that chunk's block whose index is jb
 // (mod NB), so the NB workgroups of a head bring the whole block into their
 // XCD's L2 before their own loads ask for it.  It meets the other waves at
 // their barriers (the same count), which keeps it WARM chunks ahead and no
@@ -290,14 +292,21 @@ __global__ __launch_bounds__(64 * (D / 32) + (WARM ? 64 : 0)) void state_scan_ke
 #pragma unroll
       for (int i = 0; i < SW::NL; ++i) ring[u][i] = 0;
     int acc = 0;
+    const int64_t ostride = (int64_t)n_heads * D;
     __syncthreads();
     for (int ci = c_begin; ci < c_end; ci += 3) {
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
 #pragma unroll
         for (int i = 0; i < SW::NL; ++i) acc ^= ring[u][i];
+        // the table entry is loaded before the warming loads, so using it
+        // waits for nothing issued after it
+        const bool live = ci + u < c_end;
+        const ChunkEnt ent = tab[live ? ci + u : c_end - 1];
         warm(ci + u + WARM, ring[u]);
-        __syncthreads();  // the two barriers of a step
+        __syncthreads();  // the two barriers of a step; o of the step between them
+        SS::template store_o<64>(lds, o, ostride, h, jb, __builtin_amdgcn_readfirstlane(ent.start),
+                                 live ? __builtin_amdgcn_readfirstlane(ent.len) : 0, lane);
         __syncthreads();
       }
     }
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(64 * (D / 32) + (WARM ? 64 : 0)) void state_scan_ke
   auto run_step = [&](typename SS::Ops& buf, int ci) {
     const int cn = clamp(ci + 3);
     const ChunkOut<TIO> nx = out_of(cn);
-    SS::template step<NTH>(lds, S, buf, o, ostride, h, jb, &nx, tab + cn, ci < c_end);
+    SS::template step<NTH, !WARM>(lds, S, buf, o, ostride, h, jb, &nx, tab + cn, ci < c_end);
   };
   for (int ci = c_begin; ci < c_end; ci += 3) {
     run_step(b0, ci);
