@@ -1,10 +1,10 @@
 // kda_decode.hip -- recurrent KDA decode: one token per (sequence, head) on a
 // carried fp32 state, updated in place.
 //
-// The decode form is the token recurrence itself, run once per call from the
-// state the caller passes ("prefill once, then advance one token per step from
-// the carried state"; page "Kimi-Linear: paged-incremental decode
-// (prefill-once + carried-state decode)", squash commit).  Per (n, h):
+// The decode form is the token recurrence itself, run once per call on the
+// state the caller carries over from the prefill or the previous step (page
+// "Kimi-Linear: paged-incremental decode (prefill-once + carried-state
+// decode)", squash commit).  Per (n, h):
 //     S' = Diag(exp(g)) S                 decay of each key-channel row
 //     p  = S'^T k,  r = S'^T q            two column reductions over dk
 //     u  = beta (v - p)                   delta-rule error

@@ -150,8 +150,8 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                   output_final_state: bool = True, stream=None, events=None,
                   plan: str = "auto", gate=None,
                   state_indices: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
-                  state_dtype: Optional[torch.dtype] = None, noalloc: bool = False
-                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  state_dtype: Optional[torch.dtype] = None, noalloc: bool = False,
+                  check: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked KDA prefill.  q, k: [T, Hg, dk] (Hg key heads, each shared by
     H / Hg consecutive value heads; Hg = H by default); g: [T, H, dk]; v: [T, H, dv]; beta: [T, H];
     h0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N + 1] on the device or
@@ -173,15 +173,23 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     `noalloc`: call kda_chunk_prefill_noalloc, whose workspace is the library's
     static per-device buffer (KDA_NOALLOC_WORKSPACE_BYTES) -- nothing is
     allocated for it; `workspace` and `events` must then be None, and `out`
-    (and `ht`) should be passed by callers that allocate nothing at all."""
+    (and `ht`) should be passed by callers that allocate nothing at all.
+    `cu_seqlens` is read on the device: when it is invalid (not starting at 0,
+    decreasing, or ending elsewhere than T) the kernels write neither o nor ht
+    and set the workspace's status word instead.  `check=True` reads that word
+    after the launches (this synchronises the stream) and raises KdaError if it
+    is set; without it, and with a workspace this function allocated, the
+    failure is not visible to the caller (pass `workspace` and call
+    workspace_status to read it later).  `check` needs a workspace, so it
+    cannot be combined with `noalloc`."""
     dev = q.device
     N, n_slots, out, ht = _prefill_args(q, k, v, g, beta, h0, cu_seqlens, out, ht,
                                         output_final_state, gate, state_indices, state_dtype)
     desc = prefill_desc(q, k, v, g, beta, h0, cu_seqlens, scale, chunk, out, ht, plan, gate,
                         state_indices, n_slots, qk_l2norm)
     if noalloc:
-        if workspace is not None or events is not None:
-            raise ValueError("noalloc takes no workspace and no events")
+        if workspace is not None or events is not None or check:
+            raise ValueError("noalloc takes no workspace, no events and no check")
         st = _abi.chunk_prefill_noalloc_raw(desc, _stream(stream))
         if st != _abi.KDA_OK:
             raise _abi.KdaError(st, "kda_chunk_prefill_noalloc")
@@ -202,6 +210,10 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
                                       _stream(stream), handles)
     if st != _abi.KDA_OK:
         raise _abi.KdaError(st, "kda_chunk_prefill")
+    if check:
+        st = _abi.workspace_status(workspace.data_ptr(), _stream(stream))
+        if st != _abi.KDA_OK:
+            raise _abi.KdaError(st, "kda_chunk_prefill (device status)")
     return out, ht
 
 

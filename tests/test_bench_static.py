@@ -1,6 +1,7 @@
 """bench.py on the CPU: every global name its functions use is defined (a
-renamed or deleted helper fails here rather than on the GPU), and a request
-for more than one GPU exits with a message before anything touches a device."""
+renamed or deleted helper fails here rather than on the GPU), the cache flush
+of the cold legs runs, and a request for more than one GPU exits with a
+message before anything touches a device."""
 import builtins
 import os
 import subprocess
@@ -34,3 +35,13 @@ def test_bench_refuses_several_gpus():
                        timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_bench_flush_runs():
+    """The cache-flushing read the cold legs issue, on a small CPU buffer."""
+    import importlib.util
+    import torch
+    spec = importlib.util.spec_from_file_location("bench_mod", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    bench._flusher(torch, device="cpu", nbytes=1 << 16)()

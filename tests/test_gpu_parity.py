@@ -124,6 +124,10 @@ def test_bad_cu_seqlens_reported(kda):
     good = d["cu_seqlens"]
     kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, good, out=o, workspace=ws)
     assert kda.workspace_status(ws) == 0
+    # a workspace the binding allocates itself: the status is read with check=True
+    with pytest.raises(kda.KdaError):
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, bad, check=True)
+    kda.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], None, good, check=True)
 
 
 @pytest.mark.parametrize("dtype,d,chunk,n,hi", [
