@@ -912,17 +912,6 @@ struct ScanStep {
     for (int c = 0; c < NJ; ++c) Sx[(c * KBD + w) * 64 + lane] = frag_from_d<TIO>(S[c][0], S[c][1]);
   }
 
-  // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
-  // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Expects the
-  // state slices published (publish(), then a barrier) and leaves them
-  // published for the next step.  Two workgroup barriers.  The workgroup has
-  // one wave per dk slice, so the step has no divergent branch and the
-  // compiler can count outstanding loads exactly.  NTH: threads of the
-  // workgroup.  With `nxt` set, each group of
-  // `op` is reloaded from *nxt as soon as the step has consumed it (the loads
-  // then overlap the rest of the step); nxt_ent supplies the new token range.
-  // live = false (uniform) runs the step without effect: no o rows are
-  // written and S keeps its value; the refills still happen.
   // The chunk's rows of o from the staging buffer to HBM, by NTS threads
   // (index tid): rows >= len fall outside the buffer resource; 16-byte
   // pieces, EPV values of one row each.  Runs between the two barriers of the
@@ -948,8 +937,19 @@ struct ScanStep {
     }
   }
 
-  // STORE_O: the step's own waves write o (else another wave of the
-  // workgroup calls store_o between the step's barriers).
+  // One chunk: V = U - W S, O = Ol + Q' S (rows < len written to o), then
+  // S = diag(Gam) S + Kg^T V, for each of the NJ column tiles.  Expects the
+  // state slices published (publish(), then a barrier) and leaves them
+  // published for the next step.  Two workgroup barriers.  The workgroup has
+  // one wave per dk slice, so the step has no divergent branch and the
+  // compiler can count outstanding loads exactly.  NTH: threads of the
+  // workgroup.  With `nxt` set, each group of
+  // `op` is reloaded from *nxt as soon as the step has consumed it (the loads
+  // then overlap the rest of the step); nxt_ent supplies the new token range.
+  // live = false (uniform) runs the step without effect: no o rows are
+  // written and S keeps its value; the refills still happen.  STORE_O: the
+  // step's own waves write o (else another wave of the workgroup calls
+  // store_o between the step's barriers).
   template <int NTH, bool STORE_O = true>
   static __device__ __forceinline__ void step(unsigned char* lds, f32x4 (&S)[NJ][2], Ops& op,
                                               TIO* __restrict__ o, int64_t ostride, int h,
