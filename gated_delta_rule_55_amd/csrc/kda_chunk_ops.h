@@ -80,7 +80,16 @@ struct Geo {
   static constexpr int KS_LD = D + TP;    // TIO rows of D
   static constexpr int TK_LD = KCP + TP;  // TIO rows of tokens
   static constexpr int AF_LD = C + 4;     // fp32 rows of C
-  static constexpr size_t SZ_A = cmaxz(cmaxz((size_t)C * GS_LD * 4, (size_t)2 * C * AF_LD * 4),
+  // The cumulative-sum phase has the LPC lanes of a channel scan LPC segments
+  // of SEG tokens each, rows SEG apart; rows of G are skewed by CPW floats per
+  // segment so the LPC segments of a wave's CPW channels fall in distinct
+  // banks (without the skew, GS_LD * SEG is a multiple of the 64 banks).
+  static constexpr int NWL = kLocalThreads / 64;
+  static constexpr int GS_CPW = D / NWL, GS_LPC = 64 / GS_CPW, GS_SEG = C / GS_LPC;
+  static_assert(GS_SEG >= 1 && GS_CPW % 4 == 0, "cumulative-sum tiling");
+  static __host__ __device__ constexpr int gs_row(int r) { return r * GS_LD + (r / GS_SEG) * GS_CPW; }
+  static constexpr size_t SZ_G = ((size_t)C * GS_LD + (size_t)(GS_LPC - 1) * GS_CPW) * 4;
+  static constexpr size_t SZ_A = cmaxz(cmaxz(SZ_G, (size_t)2 * C * AF_LD * 4),
                                        (size_t)D * TK_LD * sizeof(TIO));
   static constexpr size_t OFF_GS = 0;
   static constexpr size_t OFF_AS = 0;
@@ -423,7 +432,7 @@ struct ChunkLocal {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) gv[e] = live ? gv[e] : 0.f;
-        *reinterpret_cast<f32x4*>(Gs + r * GS_LD + 4 * cv) = gv;
+        *reinterpret_cast<f32x4*>(Gs + Gm::gs_row(r) + 4 * cv) = gv;
       }
     }
     if (tid < C) s_beta[tid] = tid < in.len ? to_f32(in.beta) : 0.f;
@@ -451,11 +460,12 @@ struct ChunkLocal {
       constexpr int CPW = D / NW;    // channels per wave
       constexpr int LPC = 64 / CPW;  // lanes per channel
       constexpr int SEG = C / LPC;   // tokens per lane
+      static_assert(CPW == Gm::GS_CPW && SEG == Gm::GS_SEG, "G row skew matches the scan");
       const int c = wave * CPW + lane % CPW;
       const int seg = lane / CPW;
       float gv[SEG];
 #pragma unroll
-      for (int j = 0; j < SEG; ++j) gv[j] = Gs[(seg * SEG + j) * GS_LD + c];
+      for (int j = 0; j < SEG; ++j) gv[j] = Gs[Gm::gs_row(seg * SEG + j) + c];
 #pragma unroll
       for (int j = 1; j < SEG; ++j) gv[j] += gv[j - 1];
       float before = 0.f;  // sum of the earlier segments' totals
@@ -468,7 +478,7 @@ struct ChunkLocal {
       for (int j = 0; j < SEG; ++j) {
         const int r = seg * SEG + j;
         const float G = gv[j] + before;
-        Gs[r * GS_LD + c] = G;
+        Gs[Gm::gs_row(r) + c] = G;
         if ((r & 15) == 0) rho[(r >> 4) * D + c] = G;
         if (r == C - 1) rho[TT * D + c] = G;
       }
@@ -524,7 +534,7 @@ struct ChunkLocal {
         if (((flag >> a) & 1) && i <= r) {
           const int rr = 16 * a + r, ii = 16 * a + i;
           for (int c = half * (D / 2); c < (half + 1) * (D / 2); ++c) {
-            const float f = fast_exp2(Gs[rr * GS_LD + c] - Gs[ii * GS_LD + c]);
+            const float f = fast_exp2(Gs[Gm::gs_row(rr) + c] - Gs[Gm::gs_row(ii) + c]);
             const float ki = to_f32(Lk[ii * KS_LD + c]) * f;
             sk += to_f32(Lk[rr * KS_LD + c]) * ki;
             sq += to_f32(Lq[rr * KS_LD + c]) * ki;
@@ -552,7 +562,7 @@ struct ChunkLocal {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = r0 + e;
-          const f32x2 G = *reinterpret_cast<const f32x2*>(Gs + r * GS_LD + c);
+          const f32x2 G = *reinterpret_cast<const f32x2*>(Gs + Gm::gs_row(r) + c);
           const V2 kv = *reinterpret_cast<const V2*>(Lk + r * KS_LD + c);
           const V2 qv = *reinterpret_cast<const V2*>(Lq + r * KS_LD + c);
           V2 lk2, lq2, rn2;
