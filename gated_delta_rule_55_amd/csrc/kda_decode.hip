@@ -198,6 +198,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   __shared__ float s_q[B][D], s_k[B][D], s_d[B][D], s_v[B][D], s_b[B], s_kq[B];
   __shared__ float s_u[D];
   __shared__ float s_red[2][RG][D];
+  // running-decay form of a block (see fold): k L_j, q L_j, k / L_j per token
+  // and channel, L of the block's last token, and whether the block must take
+  // the direct form instead
+  __shared__ float s_kt[B][D], s_qt[B][D], s_kh[B][D], s_L[D];
+  __shared__ int s_direct;
 
   const int tid = threadIdx.x;
   const int cq = tid % NQ;
@@ -272,24 +277,63 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
       s_b[rg] = to_f32(lb);
       s_kq[rg] = kq;
     }
+    if (tid == 0) s_direct = 0;
   };
+  // Running-decay form of a staged block of nb tokens (one thread per
+  // channel, after a barrier; a barrier must follow).  With L_j the product
+  // of the block's decays up to token j, the state is carried through the
+  // block as S_hat = S / L (per key channel), so a token needs no decay of
+  // the state: p = S_hat^T (L_j k), r = S_hat^T (L_j q), S_hat += (k / L_j) u^T,
+  // and S = L_last S_hat once at the block's end -- three operations per
+  // state value and token instead of four.  A block where some L_j leaves
+  // [2^-60, 2^60] (strong decay) keeps the direct form.
+  auto fold = [&](int nb) {
+    if (tid < D) {
+      float L = 1.f;
+      bool ok = true;
+      for (int j = 0; j < nb; ++j) {
+        L *= s_d[j][tid];
+        ok = ok && L >= 0x1p-60f && L <= 0x1p60f;
+        const float kv = s_k[j][tid];
+        s_kt[j][tid] = kv * L;
+        s_qt[j][tid] = s_q[j][tid] * L;
+        s_kh[j][tid] = kv * __builtin_amdgcn_rcpf(L);
+      }
+      s_L[tid] = L;
+      if (!ok) s_direct = 1;
+    }
+  };
+  auto block_len = [&](int64_t tb) { return t1 - tb < B ? (int)(t1 - tb) : B; };
   if (t0 < t1) {
     fetch(t0);
     stage(t0);
   }
   __syncthreads();
+  if (t0 < t1) {
+    fold(block_len(t0));
+    __syncthreads();
+  }
   for (int64_t tb = t0; tb < t1; tb += B) {
     fetch(tb + B < t1 ? tb + B : tb);  // the next block (the current one again at the end)
-    const int nb = t1 - tb < B ? (int)(t1 - tb) : B;  // tokens of this block (uniform)
+    const int nb = block_len(tb);      // tokens of this block (uniform)
+    const bool direct = s_direct != 0;
+    // the running form reads k L_j, q L_j and writes with k / L_j; the
+    // direct form decays the state first and uses k and q as they are
+    const float(*ka)[D] = direct ? s_k : s_kt;
+    const float(*qa)[D] = direct ? s_q : s_qt;
+    const float(*wa)[D] = direct ? s_k : s_kh;
 #pragma unroll 1
     for (int j = 0; j < nb; ++j) {
+      if (direct) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) s[i] *= s_d[j][rg + RG * i];
+      }
       f32x4 pk = zero4(), pq = zero4();
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        s[i] *= s_d[j][r];
-        pk += s[i] * s_k[j][r];
-        pq += s[i] * s_q[j][r];
+        pk += s[i] * ka[j][r];
+        pq += s[i] * qa[j][r];
       }
       *reinterpret_cast<f32x4*>(&s_red[0][rg][4 * cq]) = pk;
       *reinterpret_cast<f32x4*>(&s_red[1][rg][4 * cq]) = pq;
@@ -308,14 +352,19 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
       __syncthreads();
       const f32x4 u4 = *reinterpret_cast<const f32x4*>(&s_u[4 * cq]);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        s[i] += s_k[j][r] * u4;
-      }
+      for (int i = 0; i < RPT; ++i) s[i] += wa[j][rg + RG * i] * u4;
+    }
+    if (!direct) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) s[i] *= s_L[rg + RG * i];
     }
     __syncthreads();  // every token of the block has read it
     if (tb + B < t1) stage(tb + B);
     __syncthreads();
+    if (tb + B < t1) {
+      fold(block_len(tb + B));
+      __syncthreads();
+    }
   }
   if (ht) {
 #pragma unroll

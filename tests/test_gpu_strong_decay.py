@@ -96,3 +96,44 @@ def test_strong_decay_decode_matches_oracle(kda):
     eo, es = rel_l2(to_host64(o), o_ref), rel_l2(to_host64(state), st_ref)
     say(f"strong decay decode: rel-L2 o={eo:.3e} state={es:.3e}")
     assert eo <= TOL["bf16"] and es <= 1e-6
+
+
+def recurrent_block_forms(g: np.ndarray, cu: np.ndarray, block: int) -> tuple:
+    """Blocks of the recurrent prefill that take the running-decay form and
+    those that keep the direct form: a block keeps the direct form when, for
+    some (head, channel), the product of its decays up to some token leaves
+    [2^-60, 2^60] (fp64 here; the kernel decides in fp32)."""
+    running = direct = 0
+    for n in range(len(cu) - 1):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for b0 in range(s, e, block):
+            logL = np.cumsum(g[b0:min(b0 + block, e)].astype(np.float64), axis=0) / np.log(2.0)
+            if np.all((logL >= -60.0) & (logL <= 60.0)):
+                running += 1
+            else:
+                direct += 1
+    return running, direct
+
+
+@pytest.mark.parametrize("a_range,want", [((1.0, 3.0), "direct"), ((-3.0, 0.0), "running")])
+def test_recurrent_prefill_block_forms(kda, a_range, want):
+    """The recurrent prefill carries a block's state as S / L (L the running
+    product of the block's decays) unless some L leaves [2^-60, 2^60]; strong
+    decays take the direct form, the workload's the running one.  Both against
+    the oracle, with the form checked on the host (blocks of 1024 / d tokens
+    aligned to each sequence's start)."""
+    d = 128
+    inp = synth.make_inputs(63, [70, 9, 33], 3, d, dtype="bf16", h0_std=0.3, a_range=a_range)
+    running, direct = recurrent_block_forms(inp.g, inp.cu_seqlens, 1024 // d)
+    say(f"recurrent prefill a_h ~ U{a_range}: {running} running blocks, {direct} direct")
+    assert (direct if want == "direct" else running) > 0
+    dv = dev_inputs(inp)
+    o, ht = kda.recurrent_prefill(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], dv["h0"],
+                                  dv["cu_seqlens"], scale=inp.scale)
+    torch.cuda.synchronize()
+    o, ht = to_host64(o), to_host64(ht)
+    o_ref, ht_ref = oracle_prefill(inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(ht, ht_ref)
+    tok = check_tokens(o, o_ref, TOL["bf16"])
+    say(f"  rel-L2 o={eo:.3e} state={es:.3e} worst token {tok:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
