@@ -62,6 +62,7 @@ DECODE_FLOPS = 64 * 32 * (7 * 128 * 128)
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = ["gated_delta_rule_55_amd/csrc/kda_prefill.hip",
+                  "gated_delta_rule_55_amd/csrc/kda_headscan.hip",
                   "gated_delta_rule_55_amd/csrc/kda_conv.hip",
                   "gated_delta_rule_55_amd/csrc/kda_chunk_ops.h",
                   "gated_delta_rule_55_amd/csrc/kda_decode.hip",

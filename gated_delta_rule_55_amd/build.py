@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.cpp", "kda_conv.hip", "kda_decode.hip", "kda_prefill.hip"]
+SOURCES = ["kda_abi.cpp", "kda_conv.hip", "kda_decode.hip", "kda_headscan.hip", "kda_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -195,7 +195,14 @@ struct QkIn {
   int norm;
 };
 
-template <typename TIO, int D, int C, bool GATE = false>
+// HEADL: the layout the per-head scan reads.  Ol is written transposed
+// within each 16 x 16 tile (lane l16 holds token 16t + l16, lane group lg its
+// value columns 16ct + 4lg + 0..3), the layout of that scan's output tiles,
+// and the token tiles 2p, 2p + 1 of one column tile of U and of Ol sit side
+// by side for each lane, written with one 16-byte store (elements
+// ((ct TT/2 + p) 64 + lane) 8 + 4 (t & 1) + j).  Else U and Ol are in
+// accumulator order, ((t DT + ct) 64 + lane) 4 + j.
+template <typename TIO, int D, int C, bool GATE = false, bool HEADL = false>
 struct ChunkLocal {
   using Gm = Geo<TIO, D, C>;
   using FragT = typename Frag<TIO>::type;
@@ -212,9 +219,10 @@ struct ChunkLocal {
   static constexpr int NG = (C * GPR + NT - 1) / NT;  // float4 per thread of g
 
   // The chunk's inputs as this thread loads them.  Every load is issued
-  // unconditionally (rows at or past L re-read row L - 1; L >= 1) and the
-  // masking happens when the registers are staged, so the compiler can count
-  // the loads in flight and never has to wait for the whole prefetch early.
+  // unconditionally (rows at or past L fall outside the buffer resource and
+  // read 0) and the masking happens when the registers are staged, so the
+  // compiler can count the loads in flight and never has to wait for the
+  // whole prefetch early.
   struct Inputs {
     uint4 k[NV], q[NV], v[NV];
     f32x4 g[GATE ? 1 : NG];     // g, four channels per vector
@@ -277,32 +285,51 @@ struct ChunkLocal {
     const int64_t kh = (int64_t)(h / (n_heads / qk.kheads)) * D;    // key head offset
     in.tok0 = tok0;
     in.len = L;
+    // Buffer resources over the chunk's L rows of this head: the per-thread
+    // offsets depend only on the thread (no address arithmetic per item), and
+    // rows at or past L read as 0 (they are masked when staged anyway).  Byte
+    // offsets stay below 2^31 for every shape the C ABI accepts (at most
+    // 65535 heads: 64 rows x 65535 x 128 x 4 bytes < 2^31).
+    const int kst = (int)(ks * sizeof(TIO)), rst = (int)(rs * sizeof(TIO));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(const_cast<TIO*>(k) + tok0 * ks + kh, L * kst);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(const_cast<TIO*>(q) + tok0 * ks + kh, L * kst);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(const_cast<TIO*>(v) + tok0 * rs + (int64_t)h * D, L * rst);
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
       const int x0 = tid + NT * m;
       const int x = x0 < C * VPR ? x0 : C * VPR - 1;
-      const int r = min(x / VPR, L - 1), cv = x % VPR;
-      const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
-      const int64_t koff = (tok0 + r) * ks + kh;
-      in.k[m] = reinterpret_cast<const uint4*>(k + koff)[cv];
-      in.q[m] = reinterpret_cast<const uint4*>(q + koff)[cv];
-      in.v[m] = reinterpret_cast<const uint4*>(v + off)[cv];
+      const int r = x / VPR, cv = x % VPR;
+      in.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, r * kst + cv * 16, 0, 0));
+      in.q[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, r * kst + cv * 16, 0, 0));
+      in.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, r * rst + cv * 16, 0, 0));
     }
+    const int gst = (int)(rs * (GATE ? sizeof(TIO) : 4));
+    const __amdgpu_buffer_rsrc_t rg =
+        GATE ? make_rsrc(const_cast<TIO*>(dec.x) + tok0 * rs + (int64_t)h * D, L * gst)
+             : make_rsrc(const_cast<float*>(dec.g) + tok0 * rs + (int64_t)h * D, L * gst);
 #pragma unroll
     for (int m = 0; m < NG; ++m) {
       const int x0 = tid + NT * m;
       const int x = x0 < C * GPR ? x0 : C * GPR - 1;
-      const int r = min(x / GPR, L - 1), cv = x % GPR;
-      const int64_t off = (tok0 + r) * rs + (int64_t)h * D;
+      const int r = x / GPR, cv = x % GPR;
       if constexpr (GATE) {
-        in.x[m] = reinterpret_cast<const V4*>(dec.x + off)[cv];
+        if constexpr (sizeof(TIO) == 2)
+          in.x[m] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(rg, r * gst + cv * 8, 0, 0));
+        else
+          in.x[m] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(rg, r * gst + cv * 16, 0, 0));
         in.bias[m] = reinterpret_cast<const f32x4*>(dec.dt_bias + (int64_t)h * D)[cv];
       } else {
-        in.g[m] = reinterpret_cast<const f32x4*>(dec.g + off)[cv];
+        in.g[m] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, r * gst + cv * 16, 0, 0));
       }
     }
     in.ea = GATE ? __expf(dec.a_log[h]) : 1.f;
-    in.beta = beta[(tok0 + min(tid, L - 1)) * n_heads + h];
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(const_cast<TIO*>(beta) + tok0 * n_heads + h, L * n_heads * (int)sizeof(TIO));
+    if constexpr (sizeof(TIO) == 2)
+      in.beta = __builtin_bit_cast(TIO, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
+                                             rb, tid * n_heads * 2, 0, 0));
+    else
+      in.beta = __builtin_bit_cast(TIO, __builtin_amdgcn_raw_buffer_load_b32(rb, tid * n_heads * 4, 0, 0));
   }
 
   static __device__ __forceinline__ int fac_sa(int a) { return a; }
@@ -310,6 +337,35 @@ struct ChunkLocal {
   static __device__ __forceinline__ int fac_kg(int b) { return 2 * TT + b; }
   static __device__ __forceinline__ int fac_far(int a, int b) {
     return 3 * TT + (a - 2) * (a - 1) / 2 + b;
+  }
+  // Element offset of a lane's four values of U / Ol tile (t, ct).
+  static __device__ __forceinline__ size_t tile_off(int t, int ct, int lane) {
+    if constexpr (HEADL) {
+      static_assert(TT % 2 == 0, "paired token tiles");
+      return ((size_t)(ct * (TT / 2) + (t >> 1)) * 64 + lane) * 8 + 4 * (t & 1);
+    } else {
+      return ((size_t)(t * DT + ct) * 64 + lane) * 4;
+    }
+  }
+  // Store a lane's four values of U / Ol tile (t, ct); in the per-head layout
+  // the odd token tile stores both of its pair (prev: the even tile's).
+  static __device__ __forceinline__ void store_tile(TIO* base, int t, int ct, int lane, f32x4 v,
+                                                    f32x4 prev, float sc) {
+    if constexpr (HEADL && sizeof(TIO) == 2) {
+      if (t & 1) {
+        bf16x8 f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[j] = (bf16)(sc * prev[j]);
+          f[4 + j] = (bf16)(sc * v[j]);
+        }
+        *reinterpret_cast<bf16x8*>(base + tile_off(t - 1, ct, lane)) = f;
+      }
+    } else {
+      TIO* p = base + tile_off(t, ct, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = from_f32<TIO>(sc * v[j]);
+    }
   }
 
   // Scale the 8 values of a bf16 / fp32 fragment by 8 per-channel factors.
@@ -768,20 +824,20 @@ struct ChunkLocal {
         }
         ureg[t] = uacc;
         TIO* wout = out.w + ((size_t)(t * KBD + kb) * 64 + lane) * 8 + 4 * hh;
-        TIO* uout = out.u + ((size_t)(t * DT + ct) * 64 + lane) * 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const TIO wv = from_f32<TIO>(wacc[j]);
           wout[j] = wv;
           WT[(16 * ct + 4 * lg + j) * TK_LD + 16 * t + l16] = wv;
-          uout[j] = from_f32<TIO>(uacc[j]);
         }
+        store_tile(out.u, t, ct, lane, uacc, ureg[t > 0 ? t - 1 : 0], 1.f);
       }
       if constexpr (KCP != C) {
         for (int x = lane; x < 16 * (KCP - C); x += 64)
           WT[(16 * ct + x / (KCP - C)) * TK_LD + C + x % (KCP - C)] = zero_t;
       }
       wave_sync();  // this wave's W^T rows are complete
+      f32x4 oprev = zero4();  // Ol of the even token tile of a pair
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         f32x4 acc = zero4();
@@ -807,11 +863,11 @@ struct ChunkLocal {
           const FragT fa = load_frag_perm<TIO>(Aq + (16 * t + l16) * TK_LD + 32 * s, lg);
           f32x4 u1 = zero4();
           if (2 * s + 1 < TT) u1 = ureg[2 * s + 1 < TT ? 2 * s + 1 : TT - 1];
-          oacc = mma32(fa, frag_from_d<TIO>(ureg[2 * s], u1), oacc);
+          if constexpr (HEADL) oacc = mma32(frag_from_d<TIO>(ureg[2 * s], u1), fa, oacc);
+          else oacc = mma32(fa, frag_from_d<TIO>(ureg[2 * s], u1), oacc);
         }
-        TIO* oout = out.o + ((size_t)(t * DT + ct) * 64 + lane) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) oout[j] = from_f32<TIO>(scale * oacc[j]);
+        store_tile(out.o, t, ct, lane, oacc, oprev, scale);
+        oprev = oacc;
       }
     }
   }

@@ -87,6 +87,14 @@ hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t str
                           const hipEvent_t* events);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// The per-head state scan of the two-pass plan for batches (bf16, d = 128,
+// chunk 64): one workgroup per (sequence, head) over the blocks the
+// chunk-local stage wrote in the per-head layout (ntu chunks per head).
+struct ChunkEnt;
+hipError_t launch_head_scan(const PrefillArgs& a, const int* status, const int* chunk_off,
+                            const ChunkEnt* tab, const unsigned char* blocks, int ntu,
+                            hipStream_t stream);
+
 // Short causal conv (values of kda_conv_act in include/kda_conv.h).
 constexpr int CONV_NONE_ = 0;
 constexpr int CONV_SILU_ = 1;

@@ -154,13 +154,13 @@ __global__ __launch_bounds__(256) void chunk_map_kernel(const int32_t* __restric
 // Two-pass plan, stage 1: chunk-local stage for every (chunk, head).  A
 // persistent grid (one workgroup per CU) walks the (chunk, head) items; the
 // next item's inputs are loaded while the current one computes.
-template <typename TIO, int D, int C, bool GATE>
+template <typename TIO, int D, int C, bool GATE, bool HEADL>
 __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
     const TIO* __restrict__ q, const TIO* __restrict__ k, const TIO* __restrict__ v,
     DecayIn<TIO> dec, const TIO* __restrict__ beta, int n_heads, QkIn qk, float scale,
     const int* __restrict__ chunk_total, const ChunkEnt* __restrict__ tab,
     unsigned char* __restrict__ blocks, int ntu) {
-  using CL = ChunkLocal<TIO, D, C, GATE>;
+  using CL = ChunkLocal<TIO, D, C, GATE, HEADL>;
   using Gm = Geo<TIO, D, C>;
   extern __shared__ __align__(16) unsigned char lds[];
   const int n_items = *chunk_total * n_heads;
@@ -432,6 +432,33 @@ hipError_t launch_scan(const PrefillArgs& a, const int* status, const int* chunk
   return hipGetLastError();
 }
 
+// Stage 1 over every chunk of the table, blocks in the layout of the scan
+// that follows (HEADL: the per-head scan's).
+template <typename TIO, int D, int C, bool HEADL>
+hipError_t launch_local(const PrefillArgs& a, const int* chunk_total, const ChunkEnt* tab,
+                        unsigned char* blocks, int ntu, unsigned grid, hipStream_t stream) {
+  using Gm = Geo<TIO, D, C>;
+  const bool gate = a.gate.mode == GATE_KIMI_;
+  const void* fn = gate ? (const void*)chunk_local_kernel<TIO, D, C, true, HEADL>
+                        : (const void*)chunk_local_kernel<TIO, D, C, false, HEADL>;
+  hipError_t err =
+      hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Gm::LOCAL_LDS);
+  if (err != hipSuccess) return err;
+  const DecayIn<TIO> dec{a.g, static_cast<const TIO*>(a.gate.x), a.gate.a_log,
+                         a.gate.dt_bias};
+  if (gate)
+    hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, true, HEADL>), dim3(grid),
+                       dim3(kLocalThreads), Gm::LOCAL_LDS, stream, (const TIO*)a.q,
+                       (const TIO*)a.k, (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
+                       QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_total, tab, blocks, ntu);
+  else
+    hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, false, HEADL>), dim3(grid),
+                       dim3(kLocalThreads), Gm::LOCAL_LDS, stream, (const TIO*)a.q,
+                       (const TIO*)a.k, (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
+                       QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_total, tab, blocks, ntu);
+  return hipGetLastError();
+}
+
 template <typename TIO, int D, int C>
 hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t stream,
                             const hipEvent_t* ev) {
@@ -454,39 +481,30 @@ hipError_t launch_prefill_t(const PrefillArgs& a, void* workspace, hipStream_t s
     if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
 
     unsigned char* blocks = ws + L.off_blocks;
-    const bool gate = a.gate.mode == GATE_KIMI_;
-    const void* local_fn = gate ? (const void*)chunk_local_kernel<TIO, D, C, true>
-                                : (const void*)chunk_local_kernel<TIO, D, C, false>;
-    err = hipFuncSetAttribute(local_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)Gm::LOCAL_LDS);
-    if (err != hipSuccess) return err;
     int dev = 0, cus = 0;
     if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
     if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) !=
         hipSuccess)
       return err;
+    // Batches of at least as many (sequence, head) pairs as CUs take the
+    // per-head scan, which reads each block once; fewer pairs the
+    // column-block scan, whose chain of chunks is shorter per step.
+    constexpr bool kHeadBuilt = sizeof(TIO) == 2 && D == 128 && C == 64;
+    const bool head = kHeadBuilt && (int64_t)a.n_seqs * a.n_heads >= cus;
     const int64_t items = ntu * a.n_heads;
     const unsigned grid = (unsigned)(items < cus ? items : cus);
-    const DecayIn<TIO> dec{a.g, static_cast<const TIO*>(a.gate.x), a.gate.a_log,
-                           a.gate.dt_bias};
-    if (gate)
-      hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, true>), dim3(grid), dim3(kLocalThreads),
-                         Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
-                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
-                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks,
-                         (int)ntu);
-    else
-      hipLaunchKernelGGL((chunk_local_kernel<TIO, D, C, false>), dim3(grid), dim3(kLocalThreads),
-                         Gm::LOCAL_LDS, stream, (const TIO*)a.q, (const TIO*)a.k,
-                         (const TIO*)a.v, dec, (const TIO*)a.beta, a.n_heads,
-                         QkIn{a.qk.kheads, a.qk.norm}, a.scale, chunk_off + a.n_seqs, tab, blocks,
-                         (int)ntu);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (head) err = launch_local<TIO, D, C, kHeadBuilt>(a, chunk_off + a.n_seqs, tab, blocks, (int)ntu, grid, stream);
+    else err = launch_local<TIO, D, C, false>(a, chunk_off + a.n_seqs, tab, blocks, (int)ntu, grid, stream);
+    if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[2], stream)) != hipSuccess) return err;
-    switch (scan_tiles<TIO, D>(a.n_seqs, a.n_heads, cus)) {
-      case 4: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 4>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
-      case 2: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 2>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
-      default: err = launch_scan<TIO, D, C, 1>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+    if (head) {
+      err = launch_head_scan(a, status, chunk_off, tab, blocks, (int)ntu, stream);
+    } else {
+      switch (scan_tiles<TIO, D>(a.n_seqs, a.n_heads, cus)) {
+        case 4: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 4>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+        case 2: err = launch_scan<TIO, D, C, kScanTilesMax<TIO, D, 2>>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+        default: err = launch_scan<TIO, D, C, 1>(a, status, chunk_off, tab, blocks, (int)ntu, stream); break;
+      }
     }
     if (err != hipSuccess) return err;
     if (ev && (err = hipEventRecord(ev[3], stream)) != hipSuccess) return err;

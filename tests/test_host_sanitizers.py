@@ -18,7 +18,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_55_amd", "csrc")
 BUILD = os.path.join(ROOT, "gated_delta_rule_55_amd", "_build")
-OBJS = [os.path.join(BUILD, f"{n}.o") for n in ("kda_conv", "kda_decode", "kda_prefill")]
+OBJS = [os.path.join(BUILD, f"{n}.o") for n in ("kda_conv", "kda_decode", "kda_headscan", "kda_prefill")]
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-g", "-O1"]
 
 
