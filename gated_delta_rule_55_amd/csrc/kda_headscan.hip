@@ -2,9 +2,9 @@
 // recurrence with the GLA-style output fused in (page "spike(kimi-linear):
 // chunk_kda prefill AOT port -- kernel set + pinned-config recipe", commit
 // message and section Delivered), one workgroup per (sequence, head) reading
-// each chunk-local block once.  The two-pass plan takes it for batches of at
-// least as many (sequence, head) pairs as the device has CUs, where the scan
-// is bound by workspace bytes rather than by the chain of chunks.  Built with
+// each chunk-local block once.  The two-pass plan takes it for batches of more
+// (sequence, head) pairs than half the device's CUs, where the scan is bound
+// by workspace bytes rather than by the chain of chunks.  Built with
 // the default instruction scheduler: the iterative ILP scheduler used for the
 // chunk-local stage raises this kernel past the register file.
 #include "kda_chunk_ops.h"

@@ -5,7 +5,7 @@ arithmetic, so a batch must equal the same sequences run one call each (one
 sequence at H = 32 always takes the narrowest width) bit for bit, and match
 the oracle.  Batches here reach each width on a 256-CU part: 3 x 32 heads at
 d = 128 take 32 columns; at d = 64, 8 x 32 heads take 64.  At d = 128 a batch
-of at least as many (sequence, head) pairs as CUs (8 x 32 here) takes the
+of more (sequence, head) pairs than half the CUs (8 x 32 here) takes the
 per-head scan instead (tests/test_gpu_head_scan.py covers it in full): its sums
 run in the same order and its transposed Ol product rounds like the other, so
 that batch too equals the one-call runs bit for bit."""
