@@ -13,7 +13,9 @@
 namespace kda {
 namespace {
 
-// Waves of a per-head scan workgroup (4: 32 columns each; 8: 16 each).
+// Waves of a per-head scan workgroup (4: 32 columns each; 8: 16 each, two
+// per SIMD within 256 registers, measured no faster: every wave reads all of
+// W, Q' and Kg from LDS).
 constexpr int kHeadScanWaves = 4;
 
 // ---------------------------------------------------------------------------
@@ -38,8 +40,9 @@ constexpr int kHeadScanWaves = 4;
 // least one step earlier than anything issued after it.  Within a step the
 // LDS fragments of the next group of products are read before the current
 // group's MFMAs issue (scheduling barriers keep that order).  Sums run in the
-// same order as in the column-block scan; Ol is the transposed product
-// (ChunkLocal HEADL), so o can differ from that scan's in the last bit.
+// same order as in the column-block scan, and Ol, the transposed product
+// (ChunkLocal HEADL), rounds like the other: o and the states equal that
+// scan's bit for bit.
 template <int D, int C, int NW_ = 4>
 struct HeadScan {
   using Gm = Geo<bf16, D, C>;
