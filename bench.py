@@ -71,12 +71,14 @@ KERNEL_SOURCES = ["gated_delta_rule_55_amd/csrc/kda_prefill.hip",
 
 
 def _code_only(rel: str, text: str) -> str:
-    """The HIP sources without their comments (a comment edit does not change
-    a kernel, so it must not retire the counters taken on it)."""
+    """The HIP sources without their comments and with every run of white space
+    read as one space (a comment or layout edit does not change a kernel, so it
+    must not retire the counters taken on it)."""
     if not rel.endswith((".hip", ".h")):
         return text
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    return re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", " ", text).strip()
 
 
 def kernel_source_hash() -> str:
