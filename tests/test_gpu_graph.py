@@ -4,7 +4,8 @@ kda_chunk_prefill_noalloc and kda_chunk_prefill with a caller workspace are
 captured once each on a side stream and replayed three times, with other
 eager work and synchronisations between the replays; every replay must
 reproduce the eager call bit for bit.  The launches hold no memset nodes: the
-chunk map clears the status word with a kernel."""
+chunk map clears the status word with a kernel.  A batch of 256 (sequence,
+head) pairs covers the per-head scan the same way."""
 import numpy as np
 import pytest
 import torch
@@ -24,10 +25,13 @@ def kda():
     return m
 
 
-@pytest.mark.parametrize("noalloc", [True, False])
-def test_prefill_graph_replays_match_eager(kda, noalloc):
-    say(f"prefill captured in a graph, noalloc={noalloc}")
-    inp = synth.make_inputs(81, [700, 0, 333], 32, 128, dtype="bf16", h0_std=0.02, chunk=64)
+@pytest.mark.parametrize("noalloc,lengths", [
+    (True, [700, 0, 333]), (False, [700, 0, 333]),          # 96 pairs: column-block scan
+    (True, [100, 64, 0, 90, 1, 120, 77, 65]),               # 256 pairs: per-head scan
+])
+def test_prefill_graph_replays_match_eager(kda, noalloc, lengths):
+    say(f"prefill captured in a graph, noalloc={noalloc}, lengths={lengths}")
+    inp = synth.make_inputs(81, lengths, 32, 128, dtype="bf16", h0_std=0.02, chunk=64)
     d = dev_inputs(inp)
     N = len(inp.cu_seqlens) - 1
     o = torch.empty((inp.T, inp.H, inp.dk), dtype=torch.bfloat16, device="cuda")
