@@ -643,7 +643,7 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the KDA path shards by heads or sequences with no communication; "
-              "this build runs and reports a single GPU)", file=sys.stderr)
+              "the benchmark runs and reports a single GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -242,7 +242,7 @@ def seeded_lengths(seed: int, n: int, lo: int, hi: int) -> list:
     return [int(x) for x in _rng(seed, "lengths").integers(lo, hi + 1, n)]
 
 
-# The five workloads.  Config 4 is generated as 64 sequences of 1280 tokens;
+# The five workloads.  decode-64x256 is generated as 64 sequences of 1280 tokens;
 # the prefill uses tokens [0, 1024) of each and decode step s uses token
 # 1024 + s of every sequence.
 CONFIGS = {

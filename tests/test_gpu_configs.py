@@ -53,7 +53,7 @@ def check_sampled(inp, o, ht, heads, tol):
 @pytest.mark.parametrize("cfg,heads", [(0, [0, 1]), (1, [0, 9, 31]), (2, [3, 17, 30]),
                                        (3, [5, 22])])
 def test_config_prefill(kda, cfg, heads):
-    say(f"config {cfg}: {synth.CONFIGS[cfg]['name']}")
+    say(f"workload {synth.CONFIGS[cfg]['name']}")
     inp = synth.make_config(cfg)
     say(f"  T={inp.T} N={inp.N} H={inp.H} d={inp.dk} C={inp.chunk} dtype={inp.dtype}")
     o, ht = gpu_prefill(kda, inp)
@@ -61,16 +61,16 @@ def test_config_prefill(kda, cfg, heads):
 
 
 @pytest.fixture(scope="module")
-def cfg4():
-    say("config 4: generating 64 x 1280 tokens")
+def decode_inputs():
+    say("decode-64x256: generating 64 x 1280 tokens")
     return synth.make_config(4)
 
 
-def test_config4_prefill_then_decode(kda, cfg4):
+def test_decode_workload_prefill_then_decode(kda, decode_inputs):
     """Chunked prefill of tokens [0, 1024) of 64 sequences, then 256 recurrent
     decode steps on the carried state; checked against the oracle (sampled
     heads) and against a 1280-token chunked prefill on the GPU (all heads)."""
-    inp = cfg4
+    inp = decode_inputs
     N, L, P, S = 64, 1280, 1024, 256
     H, D = inp.H, inp.dk
     d = dev_inputs(inp)

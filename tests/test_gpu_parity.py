@@ -78,7 +78,7 @@ def test_decode_matches_oracle(kda, dtype, d):
 
 def test_tiny_config_prefill_vs_decode_by_decode(kda):
     """The tiny fp32 workload: chunked prefill = token-by-token decode on the GPU."""
-    say("cfg0 chunked vs decode-by-decode")
+    say("tiny-f32 chunked vs decode-by-decode")
     inp = synth.make_config(0)
     o_c, s_c = run_prefill(kda, inp)
     dev = dev_inputs(inp)

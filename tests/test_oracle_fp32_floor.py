@@ -102,6 +102,6 @@ def test_fp32_floor_per_config(cfg, heads, bound):
     o32, ht32 = oracle.prefill_f32(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"],
                                    f["cu_seqlens"], f["scale"])
     eo, es = rel(o32, o), rel(ht32, ht)
-    print(f"fp32 floor config {cfg} ({synth.CONFIGS[cfg]['name']}, heads {heads}): "
+    print(f"fp32 floor {synth.CONFIGS[cfg]['name']} (heads {heads}): "
           f"rel-L2 o={eo:.3e} state={es:.3e}", flush=True)
     assert eo < bound and es < bound
