@@ -6,8 +6,8 @@
  * leg of the benchmark do.  It shares no source with the HIP path.
  *
  * What it computes.  KDA is the gated delta rule with a decay per key channel
- * ("per-channel-decay KDA", page "spike(kimi-linear): chunk_kda prefill AOT
- * port", section Delivered).  For one (sequence, head) the state S is a
+ * (page "spike(kimi-linear): chunk_kda prefill AOT port", section
+ * Delivered).  For one (sequence, head) the state S is a
  * dk x dv matrix (rows: key channels, columns: value channels).  One token t
  * with query q, key k, value v, log-decay g (one per key channel) and write
  * strength beta updates it as
@@ -22,9 +22,10 @@
  *     o  = scale * S^T q
  * The prefill runs this token by token from the initial state h0 (zero when
  * absent) and returns the final state; the decode step is the same body run
- * once on a carried state ("prefill once, then advance one token per step from
- * the carried state", page "Kimi-Linear: paged-incremental decode
- * (prefill-once + carried-state decode)", squash commit).
+ * once on a carried state: after one prefill over the prompt, each new token
+ * updates the state it inherits from the previous call (page "Kimi-Linear:
+ * paged-incremental decode (prefill-once + carried-state decode)", squash
+ * commit).
  *
  * Arithmetic is fp64 throughout.  Every (sequence, head) chain is independent,
  * so OpenMP runs the chains in parallel; inside a chain the order of
