@@ -45,3 +45,26 @@ def test_kimi_gate_is_negative():
     assert np.all(inp.g <= 0) and np.all(np.isfinite(inp.g))
     b = synth.bf16_bits_to_f64(inp.beta)
     assert np.all((b > 0) & (b < 1))
+
+
+def test_device_inputs_recipe_and_slices():
+    """The device-side generator (run here on the CPU device): shapes, dtypes,
+    unit q/k rows, g <= 0, beta in (0, 1), the same values for the same seed,
+    and host_f64 returning one sequence's rows of the sampled heads."""
+    from synth.device_inputs import host_f64, make_device_inputs
+
+    a = make_device_inputs(5, [70, 0, 33], 4, 16, h0_std=0.02, device="cpu")
+    b = make_device_inputs(5, [70, 0, 33], 4, 16, h0_std=0.02, device="cpu")
+    assert a["q"].shape == (103, 4, 16) and a["q"].dtype == torch.bfloat16
+    assert a["g"].dtype == torch.float32 and a["h0"].shape == (3, 4, 16, 16)
+    assert a["cu_seqlens"].tolist() == [0, 70, 70, 103]
+    for x in ("q", "k", "v", "g", "beta", "h0"):
+        assert torch.equal(a[x], b[x]), x
+    n = a["q"].double().norm(dim=-1)
+    assert torch.allclose(n, torch.ones_like(n), atol=1e-2)
+    assert bool((a["g"] <= 0).all()) and bool(torch.isfinite(a["g"]).all())
+    assert bool(((a["beta"] > 0) & (a["beta"] < 1)).all())
+    f = host_f64(a, 2, [1, 3])
+    assert f["range"] == (70, 103) and f["q"].shape == (33, 2, 16)
+    assert np.array_equal(f["v"], a["v"][70:103][:, [1, 3]].double().numpy())
+    assert f["h0"].shape == (1, 2, 16, 16) and list(f["cu_seqlens"]) == [0, 33]
