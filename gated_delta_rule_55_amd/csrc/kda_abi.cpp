@@ -129,7 +129,6 @@ int check_prefill(const kda_prefill_desc* d, kda::PrefillArgs* a, bool chunked =
   const int sd = check_state_dtype(d->state_dtype, d->dtype, &a->state_bf16);
   if (sd != KDA_OK) return sd;
   a->bf16 = d->dtype == KDA_DTYPE_BF16;
-  a->plan = d->plan;
   a->n_seqs = d->n_seqs;
   a->n_heads = d->n_heads;
   a->d = d->dk;

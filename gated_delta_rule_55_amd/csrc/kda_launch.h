@@ -44,15 +44,10 @@ struct DecodeArgs {
   int n_slots = 0;
 };
 
-// Launch plans (same values as kda_plan in include/kda.h).
-constexpr int KDA_PLAN_AUTO_ = 0;
-constexpr int KDA_PLAN_FUSED_ = 1;
-constexpr int KDA_PLAN_TWO_PASS_ = 2;
-
 struct PrefillArgs {
   bool bf16;
   bool state_bf16 = false;  // h0 / ht are stored as bf16 (else fp32)
-  int n_seqs, n_heads, d, chunk, plan;
+  int n_seqs, n_heads, d, chunk;
   QkArgs qk;
   int64_t t_total;
   float scale;
