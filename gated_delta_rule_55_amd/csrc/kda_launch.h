@@ -63,8 +63,8 @@ struct PrefillArgs {
   int n_slots = 0;
 };
 
-// Recurrent (token-by-token) prefill: the prefill arguments without chunk,
-// plan or workspace.
+// Recurrent (token-by-token) prefill: the prefill arguments; it uses no chunk
+// size and no workspace.
 using RecurrentArgs = PrefillArgs;
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
