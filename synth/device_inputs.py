@@ -90,3 +90,33 @@ def host_f64(d: dict, n: int, heads: Sequence[int], t_end: Optional[int] = None)
             "beta": take(d["beta"]), "h0": h0,
             "cu_seqlens": np.array([0, e - s], dtype=np.int64), "scale": d["scale"],
             "range": (s, e)}
+
+
+def make_device_conv_inputs(seed: int, lengths: Sequence[int], dim: int, W: int,
+                            device: str = "cuda") -> dict:
+    """The short conv's recipe (conv_inputs.py) drawn on `device`: x [T, dim]
+    and carried taps [N, W - 1, dim] N(0, 1) stored bf16; weight [dim, W] and
+    bias [dim] U(-1/sqrt(W), 1/sqrt(W)) fp32; cu_seqlens int32.  Generators
+    seeded with 16 * seed + the conv stream ids."""
+    import torch
+
+    from .conv_inputs import STREAM as CSTREAM
+
+    def gen(stream):
+        g = torch.Generator(device=device)
+        g.manual_seed(16 * int(seed) + CSTREAM[stream])
+        return g
+
+    lengths = [int(x) for x in lengths]
+    T, N = int(sum(lengths)), len(lengths)
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    lim = float(W) ** -0.5
+    f32 = torch.float32
+    x = torch.randn((T, dim), generator=gen("x"), dtype=f32, device=device).to(torch.bfloat16)
+    weight = (torch.rand((dim, W), generator=gen("weight"), dtype=f32, device=device) * 2 - 1) * lim
+    bias = (torch.rand((dim,), generator=gen("bias"), dtype=f32, device=device) * 2 - 1) * lim
+    state = torch.randn((N, W - 1, dim), generator=gen("state"), dtype=f32,
+                        device=device).to(torch.bfloat16)
+    return {"x": x, "weight": weight, "bias": bias, "state": state, "cu_seqlens": cu.to(device),
+            "cu_host": cu.numpy().astype(np.int64)}

@@ -3,8 +3,9 @@
 The chunked prefill with a batch whose last sequence starts beyond element
 2^31 of q, k, v and o (and beyond byte 2^33 of g, with a workspace of ~22 GB),
 through each scan the launch can pick: the 16-column and the 32-column
-column-block scans and the per-head scan.  Then one decode step on a state of
-more than 2^31 fp32 values.  Inputs are drawn on the device
+column-block scans and the per-head scan; the token-by-token prefill on such a
+batch; one decode step on a state of more than 2^31 fp32 values; the short
+conv with x and y past element 2^31.  Inputs are drawn on the device
 (synth.device_inputs: the workload recipe's distributions, for tensors too
 large to draw on the host); the oracle checks the sequences past the boundary
 on sampled heads, from the same values copied back to the host.  Each case
@@ -116,3 +117,64 @@ def test_decode_state_past_2e31_elements(kda):
     say(f"  sequences {ns}, heads {hs}: rel-L2 o={eo:.3e} state={es:.3e}")
     assert eo <= TOL["bf16"] and es <= 1e-6
     assert np.isfinite(o_g).all()
+
+
+def test_recurrent_prefill_past_2e31_elements(kda):
+    """The token-by-token prefill over a batch whose last sequence starts past
+    element 2^31 (H = 32: 528 K tokens)."""
+    H, D = 32, 128
+    lengths = [_past(H) + 1000, 3000]
+    N = len(lengths)
+    assert lengths[0] * H * D >= ELEM_LIMIT
+    say(f"large recurrent prefill: H={H} lengths={lengths}")
+    d = make_device_inputs(311, lengths, H, D, h0_std=0.02)
+    o, ht = kda.recurrent_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                  d["cu_seqlens"], scale=d["scale"])
+    torch.cuda.synchronize()
+    heads = [0, H - 1]
+    f = host_f64(d, N - 1, heads)
+    s, e = f["range"]
+    o_ref, s_ref = oracle.prefill(f["q"], f["k"], f["v"], f["g"], f["beta"], f["h0"],
+                                  f["cu_seqlens"], f["scale"])
+    o_g = to_host64(o[s:e][:, heads])
+    s_g = to_host64(ht[N - 1:N][:, heads])
+    del o, ht, d
+    _release()
+    eo, es = rel_l2(o_g, o_ref), rel_l2(s_g, s_ref)
+    tok = check_tokens(o_g, o_ref, TOL["bf16"])
+    say(f"  last sequence, heads {heads}: rel-L2 o={eo:.3e} state={es:.3e} worst token {tok:.3e}")
+    assert eo <= TOL["bf16"] and es <= 1e-5
+
+
+def test_conv_past_2e31_elements(kda):
+    """The short conv over [q|k|v] channels (dim = 12,288, W = 4, bf16) with
+    the last sequence starting past element 2^31 of x and y; sampled channels
+    against the oracle (per-element bound), new taps bit for bit."""
+    from synth.device_inputs import make_device_conv_inputs
+
+    dim, W = 12288, 4
+    lengths = [-(-ELEM_LIMIT // dim) + 100, 500]
+    assert lengths[0] * dim >= ELEM_LIMIT
+    say(f"large conv: dim={dim} W={W} lengths={lengths}")
+    c = make_device_conv_inputs(321, lengths, dim, W)
+    new = torch.empty_like(c["state"])
+    y = kda.causal_conv1d_fwd(c["x"], c["weight"], c["bias"], cu_seqlens=c["cu_seqlens"],
+                              state_in=c["state"], state_out=new, activation="silu")
+    torch.cuda.synchronize()
+    s, e = int(c["cu_host"][1]), int(c["cu_host"][2])
+    ch = [0, 1, dim // 2, dim - 2, dim - 1]
+    host = lambda t: t.double().cpu().numpy()  # noqa: E731
+    x_s = host(c["x"][s:e][:, ch])
+    y_ref, st_ref = oracle.causal_conv1d(x_s, host(c["weight"][ch]), host(c["bias"][ch]),
+                                         np.array([0, e - s]), host(c["state"][1:2][:, :, ch]),
+                                         activation="silu")
+    y_g = host(y[s:e][:, ch])
+    st_g = host(new[1:2][:, :, ch])
+    del y, new, c
+    _release()
+    err = rel_l2(y_g, y_ref)
+    excess = float(np.max(np.abs(y_g - y_ref) - (2.0 ** -8 * np.abs(y_ref) + 1e-4)))
+    say(f"  last sequence, channels {ch}: rel-L2 y={err:.3e}, worst excess over element bound "
+        f"{excess:.2e}")
+    assert err <= TOL["bf16"] and excess <= 0.0
+    assert np.array_equal(st_g, st_ref)
