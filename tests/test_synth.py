@@ -68,3 +68,17 @@ def test_device_inputs_recipe_and_slices():
     assert f["range"] == (70, 103) and f["q"].shape == (33, 2, 16)
     assert np.array_equal(f["v"], a["v"][70:103][:, [1, 3]].double().numpy())
     assert f["h0"].shape == (1, 2, 16, 16) and list(f["cu_seqlens"]) == [0, 33]
+
+
+def test_device_conv_inputs_recipe():
+    from synth.device_inputs import make_device_conv_inputs
+
+    a = make_device_conv_inputs(7, [20, 0, 9], 24, 4, device="cpu")
+    b = make_device_conv_inputs(7, [20, 0, 9], 24, 4, device="cpu")
+    assert a["x"].shape == (29, 24) and a["x"].dtype == torch.bfloat16
+    assert a["weight"].shape == (24, 4) and a["state"].shape == (3, 3, 24)
+    for x in ("x", "weight", "bias", "state"):
+        assert torch.equal(a[x], b[x]), x
+    lim = 4 ** -0.5
+    assert float(a["weight"].abs().max()) <= lim and float(a["bias"].abs().max()) <= lim
+    assert a["cu_seqlens"].tolist() == [0, 20, 20, 29]
