@@ -53,6 +53,11 @@ BYTES_PER_TOKEN = 3 * 8192 + 16384 + 64 + 8192  # 49,216
 # With the gate fused: g (fp32, 16,384 B/token) is replaced by the raw gate x (bf16).
 BYTES_PER_TOKEN_GATED = 3 * 8192 + 8192 + 64 + 8192  # 41,024
 STATE_BYTES = 32 * 128 * 128 * 4  # one sequence's h0 or hT
+# The same bytes split by stage: the chunk-local stage reads q, k, v, g, beta;
+# the state scan writes o and reads h0 / writes hT (the workspace between
+# them is not algorithmic traffic).
+LOCAL_BYTES_PER_TOKEN = 3 * 8192 + 16384 + 64  # 41,024
+SCAN_BYTES_PER_TOKEN = 8192
 # Algorithmic flops per (64-token chunk, head) of the chunked form.
 FLOPS_PER_CHUNK_HEAD = 9_041_236
 # Decode: state read + written per step, plus the step's q, k, v, g, beta, o.
@@ -676,8 +681,23 @@ def main():
                                round(mfma_cnt / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)),
         "kernels_ms": {kname: round(v, 4) for kname, v in stage_ms.items()},
         "plan": args.plan,
-        "dominant_kernel": max(["chunk_local", "state_scan"], key=lambda kn: stage_ms[kn]),
     }
+    # Each stage against its own algorithmic bytes and its own event-timed
+    # duration (HIP events on the launch stream around each launch), with the
+    # stage's counter traffic; "dominant" is the longer stage.
+    stage_alg = {"chunk_local": T * LOCAL_BYTES_PER_TOKEN,
+                 "state_scan": T * SCAN_BYTES_PER_TOKEN + 2 * STATE_BYTES}
+    stages = {}
+    for kname, kb in stage_alg.items():
+        kach = kb / (stage_ms[kname] / 1e3) / 1e9
+        stages[kname] = {"achieved": round(kach, 1), "frac": round(kach / HBM_PEAK_GBS, 4),
+                         "ms": round(stage_ms[kname], 4), "algorithmic_bytes": kb,
+                         "traffic": measured_traffic(kname)}
+    dom = max(stages, key=lambda kn: stage_ms[kn])
+    roofline["dominant_kernel"] = dom
+    roofline["dominant"] = dict(kernel=dom, bound="hbm", peak=HBM_PEAK_GBS, unit="GB/s",
+                                **stages[dom])
+    roofline["stages"] = stages
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
