@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kLocalThreads) void chunk_local_kernel(
 // Which width is faster depends on the batch.  A step's latency grows with
 // the width (more MFMA and LDS work per workgroup between barriers), while the
 // L2 traffic for the shared operators shrinks with it; measured on MI355X at
-// H = 32, d = 128, C = 64 (ms of the scan stage):
+// H = 32, d = 128, C = 64 (ms of the scan stage, before the 16-column blocks
+// had their L2-warming wave, which took one sequence to 0.53):
 //     one 32k sequence:   NJ 1: 0.59   NJ 2: 0.69   NJ 4: 1.04
 //     four 32k sequences: NJ 1: 2.24   NJ 2: 1.48   NJ 4: 1.30
 // A single sequence is bound by its chain of steps, a batch by the shared
