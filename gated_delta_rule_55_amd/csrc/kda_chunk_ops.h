@@ -907,7 +907,11 @@ struct ScanStep {
   struct Ops {
     FragT w[NOWN][KBD], q[NOWN][KBD], k[2][KBC];
     TIO u[NJ][NOWN][4], ol[NJ][NOWN][4];
-    f32x4 gam[2];
+    // Gam of row 32w + lane % 32 of the wave's dk slice: one 4-byte load per
+    // lane; the step gathers each lane's eight rows with lane shuffles.  (Two
+    // 16-byte loads per lane would carry the same 128 bytes through the CU's
+    // address unit as 2 KB, and that unit is what the scan waits on.)
+    float gl;
     int start, len;  // the chunk's token range (set by the caller)
   };
 
@@ -952,15 +956,12 @@ struct ScanStep {
   static __device__ __forceinline__ void load_kg(Ops& op, const ChunkOut<TIO>& in) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int lg = lane >> 4;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int kc = 0; kc < KBC; ++kc)
         op.k[m][kc] = load_frag8<TIO>(in.k + ((size_t)((2 * w + m) * KBC + kc) * 64 + lane) * 8);
-    const float* Gc = in.gam + 32 * w + 4 * lg;
-    op.gam[0] = *reinterpret_cast<const f32x4*>(Gc);
-    op.gam[1] = *reinterpret_cast<const f32x4*>(Gc + 16);
+    op.gl = in.gam[32 * w + (lane & 31)];
   }
   static __device__ __forceinline__ void load(Ops& op, const ChunkOut<TIO>& in, int jb) {
     load_wq(op, in);
@@ -1035,6 +1036,13 @@ struct ScanStep {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
+    // Gam of the rows this lane's accumulators hold (32w + 16m + 4lg + j),
+    // gathered here, well before the update uses them
+    f32x4 gm[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gm[m][j] = __shfl(op.gl, 16 * m + 4 * lg + j, 64);
 
     {
 #pragma unroll
@@ -1073,7 +1081,7 @@ struct ScanStep {
       for (int c = 0; c < NJ; ++c)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          f32x4 sn = S[c][m] * op.gam[m];
+          f32x4 sn = S[c][m] * gm[m];
 #pragma unroll
           for (int kc = 0; kc < KBC; ++kc) {
             // Kg fragments are in kperm token order; read V the same way
